@@ -1,0 +1,150 @@
+"""The C-ABI library loads and exports every call include/zr.h declares, and
+the host-side validation of kernel calls rejects bad arguments without a GPU
+(no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests._lib import ROOT, LIB, load
+
+zr = load()
+HEADER = os.path.join(ROOT, "include", "zr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("zr_plan_buckets", "zr_ipg_accumulate",
+                     "zr_reduce_scatter_local", "zr_adam_partition",
+                     "zr_reduce_scatter_adam", "zr_copy_grads_in_partition",
+                     "zr_ring_rs_step", "zr_last_error", "zr_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert hasattr(lib, n)
+    # the binding wraps exactly the declared calls
+    assert sorted(zr.EXPORTED) == _declared()
+
+
+def test_version():
+    assert zr.zr_version() == 100
+
+
+class _FakeTensor:
+    """Stands in for a tensor where only an address is needed (host-side
+    validation rejects the call before anything touches the GPU)."""
+
+    def __init__(self, addr, numel, dtype="fp32"):
+        import torch
+        self._addr, self._n = addr, numel
+        self.dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def data_ptr(self):
+        return self._addr
+
+    def numel(self):
+        return self._n
+
+
+def _tiny_plan():
+    return zr.zr_plan_buckets([37, 2112, 129], [0, 0, 0], [(4, 1)], 1000)
+
+
+@pytest.mark.parametrize("kwargs,msg", [
+    (dict(group=1), "group"),
+    (dict(bucket=3), "bucket"),
+    (dict(dst=4), "dst"),
+])
+def test_reduce_rejects_bad_indices(kwargs, msg):
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    args = dict(group=0, bucket=-1, dst=-1)
+    args.update(kwargs)
+    with pytest.raises(zr.ZrError) as ei:
+        zr.zr_reduce_scatter_local(plan, args["group"], args["bucket"],
+                                   args["dst"], reps,
+                                   [_FakeTensor(0x100000, 570)] * 4, stream=0)
+    assert ei.value.status == zr.ZR_ERR_INVALID and msg in str(ei.value)
+
+
+def test_reduce_rejects_window_that_misses_a_slice():
+    plan = _tiny_plan()
+    # replica 2's window starts one element too late for partition 1
+    reps = [(_FakeTensor(0x1000 * (i + 1), 570), 570 + (i == 2)) for i in range(4)]
+    with pytest.raises(zr.ZrError) as ei:
+        zr.zr_reduce_scatter_local(plan, 0, -1, 1, reps, [_FakeTensor(0x100000, 570)], stream=0)
+    assert ei.value.status == zr.ZR_ERR_INVALID and "window" in str(ei.value)
+
+
+def test_reduce_rejects_misaligned_and_null():
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    reps[1] = _FakeTensor(0x2002, 2280)       # fp32 replica not 4-byte aligned
+    with pytest.raises(zr.ZrError):
+        zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, [_FakeTensor(0x100000, 570)] * 4, stream=0)
+    reps[1] = _FakeTensor(0, 2280)
+    with pytest.raises(zr.ZrError):
+        zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, [_FakeTensor(0x100000, 570)] * 4, stream=0)
+
+
+def test_fused_needs_one_dst_and_valid_adam():
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    with pytest.raises(zr.ZrError, match="one dst"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, -1, reps, buf, buf, buf, stream=0)
+    with pytest.raises(zr.ZrError, match="step"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, buf, buf, buf, step=0, stream=0)
+    with pytest.raises(zr.ZrError, match="betas"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, buf, buf, buf, beta1=1.0, stream=0)
+
+
+def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
+    plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
+    g = _FakeTensor(0x1000, 10, "bf16")
+    mg = _FakeTensor(0x100000, 40)
+    with pytest.raises(zr.ZrError, match="share a group"):
+        zr.zr_ipg_accumulate(plan, [0, 1], [g, g], mg, stream=0)
+    with pytest.raises(zr.ZrError, match="twice"):
+        zr.zr_ipg_accumulate(plan, [0, 0], [g, g], mg, stream=0)
+    with pytest.raises(zr.ZrError, match="past"):
+        zr.zr_ipg_accumulate(plan, [0], [g], mg, window_base=1, window_len=40, stream=0)
+
+
+def test_ring_rejects_bad_step_and_overlap():
+    bufs = [_FakeTensor(0x100000 * (i + 1), 8 * 16) for i in range(8)]
+    with pytest.raises(zr.ZrError, match="step"):
+        zr.zr_ring_rs_step(bufs, 16, 7, stream=0)
+    over = [_FakeTensor(0x100000, 64), _FakeTensor(0x100000 + 64, 64)]
+    with pytest.raises(zr.ZrError, match="overlap"):
+        zr.zr_ring_rs_step(over, 32, 0, stream=0)
+
+
+def test_copy_needs_single_bucket():
+    plan = _tiny_plan()
+    buf = _FakeTensor(0x100000, 1000)
+    with pytest.raises(zr.ZrError, match="bucket"):
+        zr.zr_copy_grads_in_partition(plan, 0, -1, 0, buf, buf, stream=0)
+
+
+def test_adam_rejects_negative_n():
+    buf = _FakeTensor(0x100000, 16)
+    with pytest.raises(zr.ZrError, match="n must"):
+        zr.zr_adam_partition(buf, buf, buf, buf, n=-1, stream=0)

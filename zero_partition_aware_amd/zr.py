@@ -1,0 +1,315 @@
+"""ctypes binding of libzr.so (the C ABI in include/zr.h).
+
+Argument marshalling only: every function here turns Python/torch arguments
+into the plain pointers and sizes of the C call of the same name, calls it,
+and raises ``ZrError`` with the library's message when the status is not
+ZR_OK.  No step of the computation happens in Python, and there is no
+fallback: if the library is missing the import fails.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built: run `python -m zero_partition_aware_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+ZR_OK, ZR_ERR_INVALID, ZR_ERR_OOM, ZR_ERR_HIP, ZR_ERR_UNSUPPORTED = range(5)
+ZR_FP32, ZR_BF16 = 0, 1
+ZR_MAX_WORLD = 64
+STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_OOM",
+                3: "ZR_ERR_HIP", 4: "ZR_ERR_UNSUPPORTED"}
+
+c_i64, c_i32, c_vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+
+
+class zr_param(ctypes.Structure):
+    _fields_ = [("numel", c_i64), ("group", c_i32)]
+
+
+class zr_group(ctypes.Structure):
+    _fields_ = [("world", c_i32), ("sp", c_i32)]
+
+
+class zr_slice(ctypes.Structure):
+    _fields_ = [("bucket", c_i64), ("group", c_i32), ("dst", c_i32),
+                ("bucket_offset", c_i64), ("flat_offset", c_i64),
+                ("part_offset", c_i64), ("numel", c_i64)]
+
+    def astuple(self):
+        return (self.bucket, self.group, self.dst, self.bucket_offset,
+                self.flat_offset, self.part_offset, self.numel)
+
+
+class zr_replica(ctypes.Structure):
+    _fields_ = [("ptr", c_vp), ("flat_base", c_i64), ("len", c_i64)]
+
+
+class zr_adam(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("step", c_i64)]
+
+
+_P = ctypes.POINTER
+_sigs = {
+    "zr_plan_buckets": (c_i32, [_P(zr_param), c_i64, _P(zr_group), c_i32, c_i64,
+                                c_i32, c_i64, _P(c_vp)]),
+    "zr_plan_free": (None, [c_vp]),
+    "zr_plan_num_buckets": (c_i32, [c_vp, _P(c_i64)]),
+    "zr_plan_num_params": (c_i32, [c_vp, _P(c_i64)]),
+    "zr_plan_partition_gradients": (c_i32, [c_vp, _P(c_i32)]),
+    "zr_plan_group_info": (c_i32, [c_vp, c_i32, _P(c_i64), _P(c_i64),
+                                   _P(c_i64), _P(ctypes.c_float)]),
+    "zr_plan_param_offset": (c_i32, [c_vp, c_i64, _P(c_i64)]),
+    "zr_plan_param_partitions": (c_i32, [c_vp, c_i64, _P(_P(c_i32)), _P(c_i32)]),
+    "zr_plan_grad_start_offset": (c_i32, [c_vp, c_i64, c_i32, _P(c_i64)]),
+    "zr_plan_slices": (c_i32, [c_vp, c_i64, _P(_P(zr_slice)), _P(c_i64)]),
+    "zr_ipg_accumulate": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
+                                  c_i64, c_i64, c_vp]),
+    "zr_reduce_scatter_local": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
+                                        c_i32, _P(c_vp), c_vp]),
+    "zr_copy_grads_in_partition": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_vp,
+                                           c_vp]),
+    "zr_adam_partition": (c_i32, [_P(zr_adam), c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_i64, c_vp]),
+    "zr_reduce_scatter_adam": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
+                                       c_i32, _P(zr_adam), c_vp, c_vp, c_vp, c_vp,
+                                       c_vp, c_vp]),
+    "zr_ring_rs_step": (c_i32, [_P(c_vp), c_i32, c_i64, c_i32, c_vp]),
+    "zr_last_error": (ctypes.c_char_p, []),
+    "zr_version": (c_i32, []),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sigs)
+
+
+class ZrError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != ZR_OK:
+        raise ZrError(status, _lib.zr_last_error().decode(errors="replace"))
+
+
+def zr_last_error():
+    return _lib.zr_last_error().decode(errors="replace")
+
+
+def zr_version():
+    return _lib.zr_version()
+
+
+# ------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None for None."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ZR_BF16
+    if t.dtype == torch.float32:
+        return ZR_FP32
+    return -1
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _adam(lr, beta1, beta2, eps, step):
+    return zr_adam(float(lr), float(beta1), float(beta2), float(eps), int(step))
+
+
+class Plan:
+    """Owns a zr_plan handle (freed with zr_plan_free)."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("plan already freed")
+        return self._h
+
+    def free(self):
+        if self._h:
+            _lib.zr_plan_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def zr_plan_buckets(numels, param_groups, groups, reduce_bucket_size,
+                    partition_gradients=0, align=1):
+    """``groups``: list of (world, sp).  Returns a Plan."""
+    n = len(numels)
+    params = (zr_param * max(n, 1))()
+    for i, (ne, g) in enumerate(zip(numels, param_groups)):
+        params[i] = zr_param(int(ne), int(g))
+    gs = (zr_group * max(len(groups), 1))()
+    for i, (w, sp) in enumerate(groups):
+        gs[i] = zr_group(int(w), int(sp))
+    out = c_vp()
+    _check(_lib.zr_plan_buckets(params, n, gs, len(groups),
+                                int(reduce_bucket_size),
+                                int(partition_gradients), int(align),
+                                ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def zr_plan_free(plan):
+    plan.free()
+
+
+def zr_plan_num_buckets(plan):
+    v = c_i64()
+    _check(_lib.zr_plan_num_buckets(plan.handle, ctypes.byref(v)))
+    return v.value
+
+
+def zr_plan_num_params(plan):
+    v = c_i64()
+    _check(_lib.zr_plan_num_params(plan.handle, ctypes.byref(v)))
+    return v.value
+
+
+def zr_plan_partition_gradients(plan):
+    v = c_i32()
+    _check(_lib.zr_plan_partition_gradients(plan.handle, ctypes.byref(v)))
+    return v.value
+
+
+def zr_plan_group_info(plan, g):
+    """(total, padded, part_numel, divisor)."""
+    t, L, P, d = c_i64(), c_i64(), c_i64(), ctypes.c_float()
+    _check(_lib.zr_plan_group_info(plan.handle, int(g), ctypes.byref(t),
+                                   ctypes.byref(L), ctypes.byref(P),
+                                   ctypes.byref(d)))
+    return t.value, L.value, P.value, d.value
+
+
+def zr_plan_param_offset(plan, p):
+    v = c_i64()
+    _check(_lib.zr_plan_param_offset(plan.handle, int(p), ctypes.byref(v)))
+    return v.value
+
+
+def zr_plan_param_partitions(plan, p):
+    ids, n = _P(c_i32)(), c_i32()
+    _check(_lib.zr_plan_param_partitions(plan.handle, int(p), ctypes.byref(ids),
+                                         ctypes.byref(n)))
+    return [ids[i] for i in range(n.value)]
+
+
+def zr_plan_grad_start_offset(plan, p, k):
+    v = c_i64()
+    _check(_lib.zr_plan_grad_start_offset(plan.handle, int(p), int(k),
+                                          ctypes.byref(v)))
+    return v.value
+
+
+def zr_plan_slices(plan, bucket=-1):
+    """List of slice tuples (bucket, group, dst, bucket_offset, flat_offset,
+    part_offset, numel)."""
+    s, n = _P(zr_slice)(), c_i64()
+    _check(_lib.zr_plan_slices(plan.handle, int(bucket), ctypes.byref(s),
+                               ctypes.byref(n)))
+    return [s[i].astuple() for i in range(n.value)]
+
+
+def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
+                      window_len=None, stream=None):
+    """grads[i]: tensor of param param_ids[i] (bf16 or fp32, all one dtype);
+    main_grad: fp32 window tensor."""
+    n = len(param_ids)
+    ids = (c_i64 * max(n, 1))(*[int(p) for p in param_ids])
+    ptrs = (c_vp * max(n, 1))(*[g.data_ptr() for g in grads])
+    dt = _dtype_code(grads[0]) if n else ZR_FP32
+    wl = main_grad.numel() if window_len is None else int(window_len)
+    _check(_lib.zr_ipg_accumulate(plan.handle, ids, ptrs, n, dt,
+                                  _ptr(main_grad), int(window_base), wl,
+                                  _stream(stream)))
+
+
+def _replicas(reps):
+    """reps: list of tensors (flat_base 0) or (tensor, flat_base) pairs."""
+    arr = (zr_replica * max(len(reps), 1))()
+    dt = None
+    for i, r in enumerate(reps):
+        t, base = (r, 0) if not isinstance(r, tuple) else r
+        arr[i] = zr_replica(t.data_ptr(), int(base), t.numel())
+        dt = _dtype_code(t) if dt is None else dt
+    return arr, (ZR_FP32 if dt is None else dt)
+
+
+def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
+                            stream=None):
+    """part_out: list of fp32 tensors (all destinations when dst == -1, else
+    the one partition)."""
+    arr, dt = _replicas(reps)
+    outs = (c_vp * max(len(part_out), 1))(*[t.data_ptr() for t in part_out])
+    _check(_lib.zr_reduce_scatter_local(plan.handle, int(group), int(bucket),
+                                        int(dst), arr, dt, outs,
+                                        _stream(stream)))
+
+
+def zr_copy_grads_in_partition(plan, group, bucket, dst, bucket_layout_src,
+                               part_out, stream=None):
+    _check(_lib.zr_copy_grads_in_partition(plan.handle, int(group), int(bucket),
+                                           int(dst), _ptr(bucket_layout_src),
+                                           _ptr(part_out), _stream(stream)))
+
+
+def zr_adam_partition(grad, master, m, v, param_bf16=None, lr=1e-3, beta1=0.9,
+                      beta2=0.999, eps=1e-8, step=1, n=None, stream=None):
+    h = _adam(lr, beta1, beta2, eps, step)
+    nn = master.numel() if n is None else int(n)
+    _check(_lib.zr_adam_partition(ctypes.byref(h), _ptr(grad), _ptr(master),
+                                  _ptr(m), _ptr(v), _ptr(param_bf16), nn,
+                                  _stream(stream)))
+
+
+def zr_reduce_scatter_adam(plan, group, bucket, dst, reps, master, m, v,
+                           param_bf16=None, grad_out=None, lr=1e-3, beta1=0.9,
+                           beta2=0.999, eps=1e-8, step=1, stream=None):
+    arr, dt = _replicas(reps)
+    h = _adam(lr, beta1, beta2, eps, step)
+    _check(_lib.zr_reduce_scatter_adam(plan.handle, int(group), int(bucket),
+                                       int(dst), arr, dt, ctypes.byref(h),
+                                       _ptr(master), _ptr(m), _ptr(v),
+                                       _ptr(param_bf16), _ptr(grad_out),
+                                       _stream(stream)))
+
+
+def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
+    n = len(rank_bufs)
+    arr = (c_vp * max(n, 1))(*[t.data_ptr() for t in rank_bufs])
+    _check(_lib.zr_ring_rs_step(arr, n, int(chunk_numel), int(step),
+                                _stream(stream)))
