@@ -1,0 +1,285 @@
+"""HIP path vs the oracle, element by element, at sizes the oracle finishes in
+seconds: several 4096-element tiles, ragged tails, misaligned pointers,
+several groups, power-of-two and other divisors, special values."""
+
+import random
+
+import numpy as np
+import pytest
+
+from oracle.adam import adam_oracle
+from oracle.bf16 import bf16_rne_oracle
+from oracle.ipg import ipg_accumulate_oracle
+from oracle.plan import plan_oracle
+from oracle.reduce import reduce_scatter_oracle
+from oracle.ring import ring_reduce_scatter_oracle, ring_order_sum
+from tests._lib import load
+from zero_partition_aware_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+zr = load()
+torch = pytest.importorskip("torch")
+from tests._gpu import (assert_bits_equal, assert_within, empty_f32,  # noqa: E402
+                        host_f32, host_u16, max_ulp, to_dev)
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def _draw(rng, n, is_bf16, sigma=1.0, special=False):
+    if special:
+        x = workloads.host_special_values(rng.integers(1 << 30), n)
+    else:
+        x = (rng.standard_normal(n) * sigma).astype(np.float32)
+    if is_bf16:
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x
+
+
+def _make_case(seed):
+    rng = random.Random(seed)
+    ng = rng.choice([1, 1, 2])
+    groups = []
+    for _ in range(ng):
+        R = rng.choice([1, 2, 3, 4, 5, 6, 8, 8, 12, 16])
+        sp = rng.choice([d for d in (1, 2, 3, 4) if R % d == 0])
+        groups.append((R, sp))
+    n = rng.randint(1, 12)
+    numels = [rng.choice([1, 3, 17, rng.randint(1, 30000)]) for _ in range(n)]
+    pg = [rng.randrange(ng) for _ in range(n)]
+    B = rng.choice([1000, 4096, 7777, 30000, 1 << 30])
+    align = rng.choice([1, 1, 8])
+    return numels, pg, groups, B, align
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("is_bf16", [False, True])
+def test_reduce_scatter_random_plans(seed, is_bf16):
+    numels, pg, groups, B, align = _make_case(seed)
+    ref = plan_oracle(numels, pg, groups, B, align)
+    plan = zr.zr_plan_buckets(numels, pg, groups, B, 0, align)
+    rng = np.random.default_rng(seed)
+    for g, info in enumerate(ref.groups):
+        if info.total == 0:
+            continue
+        reps = [_draw(rng, info.total, is_bf16) for _ in range(info.world)]
+        offs = [0] * info.world if seed % 3 else [r % 3 for r in range(info.world)]
+        dreps = [to_dev(x, o) for x, o in zip(reps, offs)]
+        want = reduce_scatter_oracle(ref, g, reps, is_bf16)
+        outs = [empty_f32(info.part_numel, offset_elems=seed % 2) for _ in range(info.world)]
+        zr.zr_reduce_scatter_local(plan, g, -1, -1, dreps, outs)
+        for k in range(info.world):
+            assert_bits_equal(host_f32(outs[k]), want[k], f"group {g} dst {k}")
+
+
+@pytest.mark.parametrize("is_bf16", [False, True])
+def test_per_bucket_per_dst_calls_compose(is_bf16):
+    w = workloads.get("tiny")
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    rng = np.random.default_rng(3)
+    reps = [_draw(rng, 2278, is_bf16) for _ in range(4)]
+    dreps = [to_dev(x) for x in reps]
+    whole = reduce_scatter_oracle(ref, 0, reps, is_bf16)
+    for k in range(4):
+        out = empty_f32(570)
+        for b in range(ref.num_buckets):
+            zr.zr_reduce_scatter_local(plan, 0, b, k, dreps, [out])
+        assert_bits_equal(host_f32(out), whole[k], f"dst {k}")
+
+
+def test_tiny_workload_with_windowed_replicas():
+    w = workloads.get("tiny")
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    reps = [workloads.host_normal(workloads.seed_for("tiny", r), 2278, 1.0) for r in range(4)]
+    whole = reduce_scatter_oracle(ref, 0, reps, False)
+    for k in range(4):
+        lo, hi = k * 570, min(2278, (k + 1) * 570)
+        win = [(to_dev(x[lo:hi]), lo) for x in reps]
+        out = empty_f32(570)
+        zr.zr_reduce_scatter_local(plan, 0, -1, k, win, [out])
+        assert_bits_equal(host_f32(out), whole[k], f"dst {k}")
+
+
+@pytest.mark.parametrize("R,sp", [(4, 1), (4, 4), (3, 1), (6, 2), (1, 1)])
+def test_special_values(R, sp):
+    numels = [4096 * 2 + 5, 3, 1000]
+    ref = plan_oracle(numels, [0, 0, 0], [(R, sp)], 5000)
+    plan = zr.zr_plan_buckets(numels, [0, 0, 0], [(R, sp)], 5000)
+    info = ref.groups[0]
+    rng = np.random.default_rng(R * 10 + sp)
+    reps = [_draw(rng, info.total, False, special=True) for _ in range(R)]
+    want = reduce_scatter_oracle(ref, 0, reps, False)
+    outs = [empty_f32(info.part_numel) for _ in range(R)]
+    with np.errstate(all="ignore"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, -1, [to_dev(x) for x in reps], outs)
+        for k in range(R):
+            assert_bits_equal(host_f32(outs[k]), want[k], f"dst {k}")
+
+
+def test_subnormal_and_overflow_probes():
+    # x/4 of a subnormal must not flush; 4 x 3e38 pre-divided stays finite.
+    vals = np.array([2.0 ** -140, 3e38, -3e38, 1e-45, -0.0], np.float32)
+    plan = zr.zr_plan_buckets([5], [0], [(4, 1)], 100)
+    ref = plan_oracle([5], [0], [(4, 1)], 100)
+    reps = [vals.copy() for _ in range(4)]
+    outs = [empty_f32(2) for _ in range(4)]
+    zr.zr_reduce_scatter_local(plan, 0, -1, -1, [to_dev(x) for x in reps], outs)
+    got = np.concatenate([host_f32(o) for o in outs])[:5]
+    want = np.concatenate([reduce_scatter_oracle(ref, 0, reps, False)[k] for k in range(4)])[:5]
+    assert_bits_equal(got, want)
+    assert got[0] == np.float32(2.0 ** -140) and got[1] == np.float32(3e38)
+    assert np.signbit(got[4])
+
+
+@pytest.mark.parametrize("n,off", [(1, 0), (4095, 0), (4096 * 3 + 7, 0), (20011, 1), (20011, 3)])
+@pytest.mark.parametrize("step", [1, 2])
+def test_adam_partition(n, off, step):
+    rng = np.random.default_rng(n + off + step)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32) if step > 1 else np.zeros(n, np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-7).astype(np.float32) if step > 1 else np.zeros(n, np.float32)
+    dg, dth, dm, dv = to_dev(g, off), to_dev(th, off), to_dev(m, off), to_dev(v, off)
+    pb = torch.zeros(n + off + 8, dtype=torch.bfloat16, device="cuda")[off: off + n]
+    zr.zr_adam_partition(dg, dth, dm, dv, pb, step=step, **HP)
+    w_th, w_m, w_v = adam_oracle(g, th, m, v, step=step, **HP)
+    gth, gm, gv = host_f32(dth), host_f32(dm), host_f32(dv)
+    assert_within(gth, w_th, what="master")
+    assert_within(gm, w_m, what="m")
+    assert_within(gv, w_v, atol=0.0, what="v")
+    # bf16 writeback = RNE of the GPU's own fp32 master, bit for bit.
+    assert np.array_equal(host_u16(pb), bf16_rne_oracle(gth))
+    print(f"adam n={n} step={step}: max ulp master {max_ulp(gth, w_th)}, "
+          f"m {max_ulp(gm, w_m)}, v {max_ulp(gv, w_v)}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("is_bf16", [False, True])
+def test_fused_equals_unfused_and_oracle(seed, is_bf16):
+    numels, pg, groups, B, align = _make_case(100 + seed)
+    ref = plan_oracle(numels, pg, groups, B, align)
+    plan = zr.zr_plan_buckets(numels, pg, groups, B, 0, align)
+    rng = np.random.default_rng(seed)
+    for g, info in enumerate(ref.groups):
+        if info.total == 0:
+            continue
+        P = info.part_numel
+        reps = [_draw(rng, info.total, is_bf16, sigma=1e-3) for _ in range(info.world)]
+        dreps = [to_dev(x) for x in reps]
+        want_g = reduce_scatter_oracle(ref, g, reps, is_bf16)
+        for k in sorted({0, info.world - 1}):
+            th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+            first = max(0, min(P, info.total - k * P))
+            th[first:] = 0.0                       # padding holds zeros
+            m = np.zeros(P, np.float32)
+            v = np.zeros(P, np.float32)
+            off = seed % 2
+            # fused
+            fth, fm, fv = to_dev(th, off), to_dev(m, off), to_dev(v, off)
+            fpb = torch.zeros(P + 8, dtype=torch.bfloat16, device="cuda")[:P]
+            fgo = empty_f32(P, off)
+            zr.zr_reduce_scatter_adam(plan, g, -1, k, dreps, fth, fm, fv, fpb, fgo, **HP)
+            # unfused
+            ug = empty_f32(P)
+            zr.zr_reduce_scatter_local(plan, g, -1, k, dreps, [ug])
+            uth, um, uv = to_dev(th), to_dev(m), to_dev(v)
+            upb = torch.zeros(P, dtype=torch.bfloat16, device="cuda")
+            zr.zr_adam_partition(ug, uth, um, uv, upb, **HP)
+            assert_bits_equal(host_f32(fgo), host_f32(ug), "grad fused vs unfused")
+            assert_bits_equal(host_f32(fgo), want_g[k], "grad vs oracle")
+            for a, b, nm in ((fth, uth, "master"), (fm, um, "m"), (fv, uv, "v")):
+                assert_bits_equal(host_f32(a), host_f32(b), nm + " fused vs unfused")
+            assert np.array_equal(host_u16(fpb), host_u16(upb))
+            w_th, w_m, w_v = adam_oracle(want_g[k], th, m, v, step=1, **HP)
+            assert_within(host_f32(fth), w_th, what="master vs oracle")
+            assert_within(host_f32(fm), w_m, what="m vs oracle")
+            assert_within(host_f32(fv), w_v, atol=0.0, what="v vs oracle")
+            assert (host_f32(fth)[first:] == 0).all()
+
+
+@pytest.mark.parametrize("is_bf16", [True, False])
+def test_ipg_random_and_integer(is_bf16):
+    numels = [4096 * 2 + 3, 5, 11111, 1, 777]
+    plan = zr.zr_plan_buckets(numels, [0] * 5, [(2, 1)], 1 << 20)
+    ref = plan_oracle(numels, [0] * 5, [(2, 1)], 1 << 20)
+    offsets = ref.param_offset
+    rng = np.random.default_rng(5)
+    for base, length in [(0, ref.groups[0].padded), (3, 9000), (8196, 11111 + 5)]:
+        mg = np.zeros(length, np.float32)
+        dmg = to_dev(mg)
+        for mb in range(4):
+            if mb % 2:
+                ints = rng.integers(-256, 257, size=sum(numels)).astype(np.float32)
+                grads = np.split(ints, np.cumsum(numels)[:-1])
+                if is_bf16:
+                    grads = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in grads]
+            else:
+                grads = [_draw(rng, n, is_bf16) for n in numels]
+            ipg_accumulate_oracle(mg, base, offsets, list(range(5)), grads, is_bf16)
+            zr.zr_ipg_accumulate(plan, list(range(5)), [to_dev(x, mb % 3) for x in grads],
+                                 dmg, window_base=base)
+        assert_bits_equal(host_f32(dmg), mg, f"window {base}+{length}")
+
+
+@pytest.mark.parametrize("n,chunk", [(8, 4096 * 3 + 5), (3, 1000), (2, 1)])
+def test_ring_steps(n, chunk):
+    rng = np.random.default_rng(n)
+    bufs = [rng.standard_normal(n * chunk).astype(np.float32) for _ in range(n)]
+    dev = [to_dev(b) for b in bufs]
+    for s in range(n - 1):
+        zr.zr_ring_rs_step(dev, chunk, s)
+    want, _ = ring_reduce_scatter_oracle(bufs)
+    for k in range(n):
+        got = host_f32(dev[k])
+        assert_bits_equal(got, want[k], f"rank {k}")
+        assert_bits_equal(got[k * chunk:(k + 1) * chunk], ring_order_sum(bufs, k))
+
+
+def test_ring_integer_equals_direct_sum():
+    n, chunk = 8, 5000
+    rng = np.random.default_rng(0)
+    bufs = [rng.integers(-1000, 1000, size=n * chunk).astype(np.float32) for _ in range(n)]
+    dev = [to_dev(b) for b in bufs]
+    for s in range(n - 1):
+        zr.zr_ring_rs_step(dev, chunk, s)
+    total = sum(b.astype(np.int64) for b in bufs).astype(np.float32)
+    for k in range(n):
+        assert np.array_equal(host_f32(dev[k])[k * chunk:(k + 1) * chunk],
+                              total[k * chunk:(k + 1) * chunk])
+
+
+def test_copy_grads_in_partition():
+    w = workloads.get("moe-16l")
+    # a shrunken MoE-like list: interleaved groups, many small buckets
+    numels = [n // 4096 + 1 for n in w.numels[:34]]
+    pg = w.param_groups[:34]
+    ref = plan_oracle(numels, pg, w.groups, 3000)
+    plan = zr.zr_plan_buckets(numels, pg, w.groups, 3000)
+    rng = np.random.default_rng(1)
+    for b in range(ref.num_buckets):
+        src = rng.standard_normal(3000).astype(np.float32)
+        dsrc = to_dev(src, b % 2)
+        for g, info in enumerate(ref.groups):
+            for k in range(info.world):
+                out = empty_f32(info.part_numel)
+                zr.zr_copy_grads_in_partition(plan, g, b, k, dsrc, out)
+                want = np.full(info.part_numel, np.nan, np.float32)
+                for s in ref.slices:
+                    if s.bucket == b and s.group == g and s.dst == k:
+                        want[s.part_offset:s.part_offset + s.numel] = \
+                            src[s.bucket_offset:s.bucket_offset + s.numel]
+                assert_bits_equal(host_f32(out), want, f"bucket {b} group {g} dst {k}")
+
+
+def test_invalid_call_leaves_outputs_untouched():
+    plan = zr.zr_plan_buckets([100], [0], [(2, 1)], 64)
+    reps = [to_dev(np.ones(100, np.float32)) for _ in range(2)]
+    out = empty_f32(50, fill=7.0)
+    short = [(to_dev(np.ones(10, np.float32)), 0)] * 2
+    with pytest.raises(zr.ZrError):
+        zr.zr_reduce_scatter_local(plan, 0, -1, 0, short, [out])
+    assert (host_f32(out) == 7.0).all()
+    zr.zr_reduce_scatter_local(plan, 0, -1, 0, reps, [out])
+    assert (host_f32(out) == 1.0).all()

@@ -1,0 +1,200 @@
+"""HIP path at the workloads' full sizes, checked on sampled outputs that the
+oracle computes one by one from the gathered inputs (bit-exact for reduced
+gradients and IPG sums, within rel 1e-6 / abs 1e-7 for Adam)."""
+
+import gc
+
+import numpy as np
+import pytest
+
+from oracle.adam import adam_oracle
+from oracle.bf16 import bf16_rne_oracle
+from oracle.ipg import ipg_accumulate_oracle
+from oracle.plan import plan_oracle
+from oracle.reduce import rank_order_mean
+from oracle.ring import ring_order_sum
+from tests._lib import load
+from zero_partition_aware_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+zr = load()
+torch = pytest.importorskip("torch")
+from tests._gpu import assert_bits_equal, assert_within, host_f32, host_u16  # noqa: E402
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+DEV = "cuda"
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _sample(P, n, seed, slices=()):
+    """Random partition offsets plus the edges of every slice and tile."""
+    rng = np.random.default_rng(seed)
+    idx = set(rng.integers(0, P, size=n).tolist())
+    idx.update(range(0, min(P, 4100)))
+    idx.update(range(max(0, P - 4100), P))
+    for s in slices:
+        for e in (s.part_offset, s.part_offset + s.numel - 1):
+            idx.update(range(max(0, e - 9), min(P, e + 10)))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def _gather(t, idx):
+    """Values of device tensor t at host indices idx, as host numpy
+    (fp32, or uint16 patterns for bf16)."""
+    g = t[torch.from_numpy(idx).to(DEV)]
+    return host_u16(g) if g.dtype == torch.bfloat16 else host_f32(g)
+
+
+def _check_fused(reps_s, is_bf16, D, th_s, master, m, v, pbf16, gout, idx):
+    want_g = rank_order_mean([(_widen(x) if is_bf16 else x) for x in reps_s], D)
+    assert_bits_equal(_gather(gout, idx), want_g, "reduced gradient")
+    z = np.zeros_like(th_s)
+    w_th, w_m, w_v = adam_oracle(want_g, th_s, z, z, step=1, **HP)
+    g_th = _gather(master, idx)
+    assert_within(g_th, w_th, what="master")
+    assert_within(_gather(m, idx), w_m, what="m")
+    assert_within(_gather(v, idx), w_v, atol=0.0, what="v")
+    assert np.array_equal(_gather(pbf16, idx), bf16_rne_oracle(g_th))
+
+
+def _widen(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_gpt2_small_fused_every_rank():
+    name = "gpt2-small"
+    w = workloads.get(name)
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    info = ref.groups[0]
+    T, P, R = info.total, info.part_numel, info.world
+    reps = [workloads.device_normal(workloads.seed_for(name, r), T, w.grad_sigma, DEV, "bf16")
+            for r in range(R)]
+    for k in range(R):
+        master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                         w.master_sigma, DEV)
+        idx = _sample(P, 20000, k, [s for s in ref.slices if s.dst == k])
+        th_s = _gather(master, idx)
+        m = torch.zeros(P, device=DEV)
+        v = torch.zeros(P, device=DEV)
+        pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+        gout = torch.empty(P, device=DEV)
+        zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, master, m, v, pbf16, gout, **HP)
+        reps_s = [_gather(r_, k * P + idx) for r_ in reps]
+        _check_fused(reps_s, True, info.divisor, th_s, master, m, v, pbf16, gout, idx)
+        print(f"gpt2-small rank {k}: {idx.size} sampled elements ok")
+    del reps
+    _free()
+
+
+def test_llama3_8b_ipg_then_fused_rank_windows():
+    name = "llama3-8b"
+    w = workloads.get(name)
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    info = ref.groups[0]
+    P, R = info.part_numel, info.world
+    for k in (0, R - 1):
+        lo, hi = k * P, (k + 1) * P
+        pids = [p for p in range(len(w.numels))
+                if ref.param_offset[p] < hi and ref.param_offset[p] + w.numels[p] > lo]
+        starts = np.cumsum([0] + [w.numels[p] for p in pids])
+        buf_n = int(starts[-1])
+        idx = _sample(P, 20000, 10 + k, [s for s in ref.slices if s.dst == k])
+        flat = lo + idx
+        # position of each sampled flat element inside the gradient buffer
+        offs = np.array([ref.param_offset[p] for p in pids], dtype=np.int64)
+        which = np.searchsorted(offs, flat, side="right") - 1
+        pos = starts[which] + (flat - offs[which])
+        mgs = [torch.zeros(P, device=DEV) for _ in range(R)]
+        mg_s = [np.zeros(idx.size, np.float32) for _ in range(R)]
+        gbuf = torch.empty(buf_n, dtype=torch.bfloat16, device=DEV)
+        views = [gbuf[int(starts[i]):int(starts[i + 1])] for i in range(len(pids))]
+        for mu in range(w.micro_batches):
+            for r in range(R):
+                workloads.device_normal(workloads.seed_for(name, r, mu), buf_n,
+                                        w.grad_sigma, DEV, "bf16", out=gbuf)
+                zr.zr_ipg_accumulate(plan, pids, views, mgs[r], window_base=lo)
+                gs = _gather(gbuf, pos)
+                # oracle on the samples: one add per micro-batch, in order
+                ipg_accumulate_oracle(mg_s[r], 0, [0], [0], [gs], True)
+            print(f"llama3-8b rank {k}: micro-batch {mu} accumulated", flush=True)
+        for r in range(R):
+            assert_bits_equal(_gather(mgs[r], idx), mg_s[r], f"IPG replica {r}")
+        del gbuf, views
+        _free()
+        master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                         w.master_sigma, DEV)
+        th_s = _gather(master, idx)
+        m = torch.zeros(P, device=DEV)
+        v = torch.zeros(P, device=DEV)
+        pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+        gout = torch.empty(P, device=DEV)
+        reps = [(mg, lo) for mg in mgs]
+        zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, master, m, v, pbf16, gout, **HP)
+        _check_fused(mg_s, False, info.divisor, th_s, master, m, v, pbf16, gout, idx)
+        print(f"llama3-8b rank {k}: {idx.size} sampled elements ok")
+        del mgs, reps, master, m, v, pbf16, gout
+        _free()
+
+
+def test_moe_two_groups_fused_and_bucketed():
+    name = "moe-16l"
+    w = workloads.get(name)
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    for g, info in enumerate(ref.groups):
+        T, P, R = info.total, info.part_numel, info.world
+        reps = [workloads.device_normal(workloads.seed_for(name, r + 100 * g), T,
+                                        w.grad_sigma, DEV) for r in range(R)]
+        k = R - 1
+        master = workloads.device_normal(workloads.seed_for(name, 10 * g + k, master=True), P,
+                                         w.master_sigma, DEV)
+        mb = master.clone()
+        idx = _sample(P, 20000, g, [s for s in ref.slices if s.dst == k and s.group == g])
+        th_s = _gather(master, idx)
+        m, v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
+        pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+        gout = torch.empty(P, device=DEV)
+        zr.zr_reduce_scatter_adam(plan, g, -1, k, reps, master, m, v, pbf16, gout, **HP)
+        reps_s = [_gather(r_, k * P + idx) for r_ in reps]
+        _check_fused(reps_s, False, info.divisor, th_s, master, m, v, pbf16, gout, idx)
+        # The bucketed path (one fused call per bucket) gives the same bits.
+        mb_m, mb_v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
+        mb_p = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+        for b in range(ref.num_buckets):
+            zr.zr_reduce_scatter_adam(plan, g, b, k, reps, mb, mb_m, mb_v, mb_p, None, **HP)
+        torch.cuda.synchronize()
+        assert torch.equal(mb.view(torch.int32), master.view(torch.int32))
+        assert torch.equal(mb_v.view(torch.int32), v.view(torch.int32))
+        assert torch.equal(mb_p.view(torch.int16), pbf16.view(torch.int16))
+        print(f"moe group {g} rank {k}: {idx.size} sampled elements ok, bucketed == whole")
+        del reps, master, mb, m, v, pbf16, gout, mb_m, mb_v, mb_p
+        _free()
+
+
+def test_ring_1gib_eight_ranks():
+    cfg = workloads.RING_1GIB
+    N, M = cfg["ranks"], cfg["elems_per_rank"]
+    C = M // N
+    bufs = [workloads.device_normal(workloads.seed_for("ring-1gib", r), M, cfg["sigma"], DEV)
+            for r in range(N)]
+    rng = np.random.default_rng(3)
+    j = np.unique(np.concatenate([rng.integers(0, C, 20000), np.arange(4100),
+                                  np.arange(C - 4100, C)]))
+    S = j.size
+    # samples[r][c*S:(c+1)*S]: rank r's chunk c at the sampled offsets
+    samples = [np.concatenate([_gather(b, c * C + j) for c in range(N)]) for b in bufs]
+    for s in range(N - 1):
+        zr.zr_ring_rs_step(bufs, C, s)
+    for k in range(N):
+        assert_bits_equal(_gather(bufs[k], k * C + j), ring_order_sum(samples, k),
+                          f"rank {k} chunk {k}")
+    del bufs
+    _free()

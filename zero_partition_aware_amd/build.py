@@ -55,8 +55,12 @@ def build(verbose=False):
     out += _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
                  os.path.join(CSRC, "zr_kernels.hip"), "-o", kern_o])
     tmp = LIB + ".tmp"
-    out += _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}",
-                 plan_o, kern_o, "-o", tmp])
+    # The HIP runtime is a dependency by soname (libamdhip64.so.7): in a
+    # process that already holds torch's copy of the runtime (same soname) the
+    # loader reuses it; standalone, RUNPATH finds the ROCm installation's.
+    out += _run(["g++", "-shared", "-fPIC", plan_o, kern_o,
+                 "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
+                 "-Wl,--no-undefined", "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print(out)

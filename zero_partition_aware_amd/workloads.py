@@ -19,7 +19,8 @@ loaded; gradients are random stand-ins for backward gradients):
   sequence-parallel 2; fp32 grads; bucket 5e6.
 
 Seed scheme: replica r, micro-batch mu of workload c gets
-``c*100000 + mu*1000 + r``; the master weights get ``c*100000 + 99999``.
+``c*100000 + mu*1000 + r``; rank k's master weights get
+``c*100000 + 99000 + k``.
 """
 
 from dataclasses import dataclass
@@ -106,9 +107,11 @@ RING_1GIB = {"ranks": 8, "elems_per_rank": (1 << 30) // 4, "sigma": 1.0}
 
 
 def seed_for(name, replica=0, micro_batch=0, master=False):
+    """Seed of replica ``replica``'s micro-batch ``micro_batch`` gradients, or
+    (``master=True``) of rank ``replica``'s master weights."""
     c = WORKLOAD_IDS[name]
     if master:
-        return c * 100000 + 99999
+        return c * 100000 + 99000 + replica
     return c * 100000 + micro_batch * 1000 + replica
 
 

@@ -16,7 +16,30 @@ LIB_PATH = os.path.join(_HERE, "libzr.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built: run `python -m zero_partition_aware_amd.build`")
+
+# torch ships its own HIP runtime under the same soname as ROCm's.  Import it
+# first so that the library binds to the runtime torch already holds: two HIP
+# runtimes in one process do not share devices, streams or memory.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    torch = None
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_loaded():
+    try:
+        with open("/proc/self/maps") as fh:
+            return sorted({ln.split()[-1] for ln in fh
+                           if "libamdhip64" in ln and "/" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({_hip_runtimes_loaded()}); import torch before any "
+                      "other HIP library")
 
 ZR_OK, ZR_ERR_INVALID, ZR_ERR_OOM, ZR_ERR_HIP, ZR_ERR_UNSUPPORTED = range(5)
 ZR_FP32, ZR_BF16 = 0, 1
