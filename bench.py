@@ -18,7 +18,6 @@ partition.  Other workloads (``--workload``) are for characterisation.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,15 +32,6 @@ HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for rel in ("zero_partition_aware_amd/csrc/zr_kernels.hip",
-                "zero_partition_aware_amd/build.py"):
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_for(kernel_key):
     """HBM bytes per launch measured by rocprofv3 counters for this exact
     kernel source, or None when absent or stale."""
@@ -50,20 +40,29 @@ def traffic_for(kernel_key):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
+    from zero_partition_aware_amd.build import source_hash
     entry = t.get(kernel_key)
-    if not entry or entry.get("kernel_src_sha") != kernel_source_hash():
+    if not entry or entry.get("kernel_src_sha") != source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
 
 
 class Timer:
-    """Per-launch HIP events on the launch stream plus a step-level clock."""
+    """Counts launches per kernel label; when a step launches more than one
+    kind of kernel it also brackets every launch with HIP events (on the
+    launch stream, torch's current stream) to split the time per kernel."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, per_launch):
         self.torch = torch
+        self.per_launch = per_launch
         self.ev = []
+        self.count = {}
 
     def launch(self, fn, label):
+        self.count[label] = self.count.get(label, 0) + 1
+        if not self.per_launch:
+            fn()
+            return
         a = self.torch.cuda.Event(enable_timing=True)
         b = self.torch.cuda.Event(enable_timing=True)
         a.record()
@@ -292,25 +291,37 @@ def main():
         setup(torch, zr, workloads)
     torch.cuda.synchronize()
 
-    warm = Timer(torch)
+    per_launch = len(launch_bytes) > 1
+    warm = Timer(torch, per_launch)
     for i in range(args.warmup):
         step(i, warm)
     torch.cuda.synchronize()
 
-    timer = Timer(torch)
+    timer = Timer(torch, per_launch)
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region0.record()
     for i in range(args.steps):
         step(args.warmup + i, timer)
+    region1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    region_s = 1e-3 * region0.elapsed_time(region1)
 
-    ms = timer.per_label_ms()
-    launches = {k: {"count": len(v), "avg_us": 1e3 * sum(v) / len(v),
-                    "achieved_GBps": launch_bytes[k] / (1e-3 * sum(v) / len(v)) / 1e9}
-                for k, v in ms.items()}
-    # GPU-side time of a step: sum of its launches' event-timed durations.
-    gpu_step_s = sum(1e-3 * sum(v) for v in ms.values()) / args.steps
+    if per_launch:
+        ms = timer.per_label_ms()
+        per_label_s = {k: (len(v), 1e-3 * sum(v) / len(v)) for k, v in ms.items()}
+    else:
+        # One kernel per step: its average launch duration is the event-timed
+        # region divided by the launches in it (gaps between launches count).
+        (label, n), = timer.count.items()
+        per_label_s = {label: (n, region_s / n)}
+    launches = {k: {"count": n, "avg_us": 1e6 * t,
+                    "achieved_GBps": launch_bytes[k] / t / 1e9}
+                for k, (n, t) in per_label_s.items()}
+    gpu_step_s = region_s / args.steps
     wall_step_s = elapsed / args.steps
     dom = launches[dominant]
     roof = {"bound": "hbm", "achieved": round(dom["achieved_GBps"], 1), "peak": PEAK_GBS,
@@ -334,7 +345,7 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "pct_of_peak": round(100 * bytes_per_step / wall_step_s / 1e9 / PEAK_GBS, 2),
-        "gpu_event_GBps": round(bytes_per_step / gpu_step_s / 1e9, 1),
+        "gpu_region_GBps": round(bytes_per_step / gpu_step_s / 1e9, 1),
         "elements_per_s": round(elems_per_step / wall_step_s),
         "launches": launches,
         "roofline": roof,

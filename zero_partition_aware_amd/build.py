@@ -33,6 +33,17 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def source_hash():
+    """Short hash of the kernel source and build flags: counter measurements
+    are only valid for the exact code they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in (os.path.join(CSRC, "zr_kernels.hip"), os.path.abspath(__file__)):
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def _run(cmd):
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                           text=True)

@@ -3,15 +3,24 @@
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
 // LDS staging and no MFMA.  Work is cut into tiles of kTileElems elements of
 // one "segment" (a merged slice of the plan, a param's piece of an IPG
-// window, a ring chunk); a workgroup walks tiles with a grid-stride loop and
-// finds each tile's segment by a binary search over per-segment tile offsets.
-// Inside a tile, each lane handles groups of VE consecutive elements, VE being
-// one 16-byte load of the input type (8 bf16 or 4 fp32), so that every load
-// instruction of a wavefront covers 1 KiB of contiguous memory.  A group is
-// taken on the vector path when it lies wholly inside the segment and every
-// stream it touches is 16-byte aligned there; the alignment phase is derived
-// per segment from the actual addresses, so any element-aligned pointers
-// work, and groups at ragged segment edges fall back to element-wise code.
+// window, a ring chunk); by default every workgroup takes exactly one tile, so
+// the hardware dispatcher hands tiles out in address order and the set of
+// DRAM pages being touched at any moment stays compact.  A workgroup finds its
+// tile's segment by a binary search over per-segment tile offsets.
+//
+// Inside a tile each lane owns "slots" of four consecutive elements, and the
+// 64 lanes of a wavefront own 64 consecutive slots, so every load or store
+// instruction of one stream covers one contiguous range (1 KiB of fp32, 512 B
+// of bf16): stores fill whole cache lines and never leave partially written
+// lines behind.  All loads of a tile's slots are issued before any arithmetic.
+// A slot takes the vector path when it lies wholly inside its segment and
+// every stream is aligned there (16 B for fp32, 8 B for bf16); the alignment
+// phase is derived per segment from the actual addresses, so any
+// element-aligned pointers work, and slots at ragged segment edges fall back
+// to element-wise code.  Loads and stores carry the non-temporal hint: every
+// byte is touched once.  (With stores that fill only part of a line per
+// instruction the same hint costs half the bandwidth, so the whole-line store
+// layout above is what makes it pay.)
 //
 // Arithmetic follows the method's definition exactly: each replica's value is
 // divided by D first, the quotients are summed in rank order 0..R-1 starting
@@ -39,8 +48,36 @@ using zr::fail;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int64_t kTileElems = 4096;
+// Launch-shape constants (compile-time; the defaults are the tuned values).
+#ifndef ZR_TILE_ELEMS
+#define ZR_TILE_ELEMS 2048
+#endif
+#ifndef ZR_THREADS
+#define ZR_THREADS 256
+#endif
+// Workgroups per CU when a grid-stride loop is wanted; 0 = one tile per WG.
+#ifndef ZR_GRID_PER_CU
+#define ZR_GRID_PER_CU 0
+#endif
+// Non-temporal hints on the single-touch streams (measured: +7% on the fused
+// step once every store instruction writes whole cache lines).
+#ifndef ZR_NT_LOADS
+#define ZR_NT_LOADS 1
+#endif
+#ifndef ZR_NT_STORES
+#define ZR_NT_STORES 1
+#endif
+// 1: the vector path of the reduce kernels uses buffer instructions with a
+// per-tile resource (base = the tile's first element of each stream).
+#ifndef ZR_BUFFER_OPS
+#define ZR_BUFFER_OPS 0
+#endif
+constexpr int kThreads = ZR_THREADS;
+constexpr int64_t kTileElems = ZR_TILE_ELEMS;
+constexpr int VE = 4;  // elements per lane slot
+constexpr int kSlots = static_cast<int>(kTileElems / (kThreads * VE));
+static_assert(kSlots >= 1 && kTileElems == int64_t(kSlots) * kThreads * VE,
+              "a tile must be a whole number of lane slots");
 constexpr int kIpgMaxSegs = 48;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -51,36 +88,74 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ T ld_stream(const void* p) {
+#if ZR_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+#else
+  return *reinterpret_cast<const T*>(p);
+#endif
 }
 template <typename T>
 __device__ __forceinline__ void st_stream(void* p, T v) {
+#if ZR_NT_STORES
   __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+#else
+  *reinterpret_cast<T*>(p) = v;
+#endif
+}
+
+// Slot loads/stores relative to a per-tile stream base (uniform across the
+// workgroup) at a per-lane byte offset.
+constexpr int kTileBytes = static_cast<int>(kTileElems) * 4;
+template <typename V>
+__device__ __forceinline__ V ld_tile(uint64_t base, uint32_t off) {
+#if ZR_BUFFER_OPS
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0,
+                                                    kTileBytes, 0x00020000);
+  if constexpr (sizeof(V) == 8)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, ZR_NT_LOADS ? 2 : 0));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, ZR_NT_LOADS ? 2 : 0));
+#else
+  return ld_stream<V>(reinterpret_cast<const void*>(base + off));
+#endif
+}
+template <typename V>
+__device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
+#if ZR_BUFFER_OPS
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0,
+                                                    kTileBytes, 0x00020000);
+  if constexpr (sizeof(V) == 8)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, ZR_NT_STORES ? 2 : 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, ZR_NT_STORES ? 2 : 0);
+#else
+  st_stream<V>(reinterpret_cast<void*>(base + off), v);
+#endif
 }
 
 __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
   return (addr & (bytes - 1)) == 0;
 }
 
-// Input element types: bf16 as its 16-bit pattern, or fp32.
+// Input element types: bf16 as its 16-bit pattern, or fp32.  Vec holds one
+// slot (four elements).
 template <typename InT> struct In;
 template <> struct In<uint16_t> {
-  static constexpr int VE = 8;  // elements per 16-byte load
+  using Vec = u32x2;
   __device__ static __forceinline__ float widen(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
-  __device__ static __forceinline__ void unpack(u32x4 w, float* x) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
+  __device__ static __forceinline__ void unpack(Vec w, float* x) {
+    x[0] = __uint_as_float(w[0] << 16);
+    x[1] = __uint_as_float(w[0] & 0xffff0000u);
+    x[2] = __uint_as_float(w[1] << 16);
+    x[3] = __uint_as_float(w[1] & 0xffff0000u);
   }
 };
 template <> struct In<float> {
-  static constexpr int VE = 4;
+  using Vec = u32x4;
   __device__ static __forceinline__ float widen(float v) { return v; }
-  __device__ static __forceinline__ void unpack(u32x4 w, float* x) {
+  __device__ static __forceinline__ void unpack(Vec w, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
   }
@@ -112,6 +187,32 @@ __device__ __forceinline__ void adam_elem(const AdamConsts& k, float g,
   th = th - upd;
   m = m1;
   v = v1;
+}
+
+// Adam on one slot held in registers; writes master, m, v and the optional
+// bf16 param / reduced-gradient copies of that slot.  Each destination is a
+// per-tile stream base plus the slot's byte offset (o4 for fp32 streams, o2
+// for the bf16 param); a zero base means "not written".
+__device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
+                                          f32x4 th, f32x4 mm, f32x4 vv,
+                                          uint64_t master, uint64_t m, uint64_t v,
+                                          uint64_t pbf16, uint64_t gout,
+                                          uint32_t o4, uint32_t o2) {
+  float t[4], a[4], b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    t[e] = th[e];
+    a[e] = mm[e];
+    b[e] = vv[e];
+    adam_elem(k, g[e], t[e], a[e], b[e]);
+  }
+  st_tile<f32x4>(master, o4, f32x4{t[0], t[1], t[2], t[3]});
+  st_tile<f32x4>(m, o4, f32x4{a[0], a[1], a[2], a[3]});
+  st_tile<f32x4>(v, o4, f32x4{b[0], b[1], b[2], b[3]});
+  if (gout) st_tile<f32x4>(gout, o4, f32x4{g[0], g[1], g[2], g[3]});
+  if (pbf16)
+    st_tile<u32x2>(pbf16, o2, u32x2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
+                                    bf16_rne(t[2]) | (bf16_rne(t[3]) << 16)});
 }
 
 // ------------------------------------------------------ reduce (+ Adam) ---
@@ -149,37 +250,37 @@ __device__ __forceinline__ float predivide(const RedArgs& a, float x) {
   else return x * a.inv_divisor;
 }
 
-// Reduced gradient of VE consecutive flat elements starting at f (vector path).
+// Rank-ordered pre-divided sum of one slot from its loaded replica vectors.
 template <typename InT, int R, bool kDiv>
-__device__ __forceinline__ void reduce_vec(const RedArgs& a, int rr, int64_t f,
-                                           float* acc) {
-  constexpr int VE = In<InT>::VE;
+__device__ __forceinline__ void reduce_slot(const RedArgs& a,
+                                            const typename In<InT>::Vec* w,
+                                            float* acc) {
+  float x[4];
+  In<InT>::unpack(w[0], x);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = (R == 1) ? x[e] : predivide<kDiv>(a, x[e]);
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    In<InT>::unpack(w[r], x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] + predivide<kDiv>(a, x[e]);
+  }
+}
+
+// Same for a run-time replica count (loads issued inside the rank loop).
+template <typename InT, bool kDiv>
+__device__ __forceinline__ void reduce_slot_rt(const RedArgs& a, int rr, int64_t f,
+                                               float* acc) {
+  using Vec = typename In<InT>::Vec;
   const uint64_t off = static_cast<uint64_t>(f) * sizeof(InT);
-  if constexpr (R > 0) {
-    u32x4 w[R];
+  float x[4];
+  In<InT>::unpack(ld_stream<Vec>(reinterpret_cast<const void*>(a.in[0] + off)), x);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      w[r] = ld_stream<u32x4>(reinterpret_cast<const void*>(a.in[r] + off));
-    float x[VE];
-    In<InT>::unpack(w[0], x);
+  for (int e = 0; e < 4; ++e) acc[e] = (rr == 1) ? x[e] : predivide<kDiv>(a, x[e]);
+  for (int r = 1; r < rr; ++r) {
+    In<InT>::unpack(ld_stream<Vec>(reinterpret_cast<const void*>(a.in[r] + off)), x);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[e] = (R == 1) ? x[e] : predivide<kDiv>(a, x[e]);
-#pragma unroll
-    for (int r = 1; r < R; ++r) {
-      In<InT>::unpack(w[r], x);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[e] = acc[e] + predivide<kDiv>(a, x[e]);
-    }
-  } else {
-    float x[VE];
-    In<InT>::unpack(ld_stream<u32x4>(reinterpret_cast<const void*>(a.in[0] + off)), x);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[e] = (rr == 1) ? x[e] : predivide<kDiv>(a, x[e]);
-    for (int r = 1; r < rr; ++r) {
-      In<InT>::unpack(ld_stream<u32x4>(reinterpret_cast<const void*>(a.in[r] + off)), x);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[e] = acc[e] + predivide<kDiv>(a, x[e]);
-    }
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] + predivide<kDiv>(a, x[e]);
   }
 }
 
@@ -197,35 +298,40 @@ __device__ __forceinline__ float reduce_one(const RedArgs& a, int rr, int64_t f)
   return acc;
 }
 
+// Tile -> segment by binary search over the segments' first-tile indices.
+__device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <typename InT, int R, bool kDiv, bool kFused>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const RedArgs a) {
-  constexpr int VE = In<InT>::VE;
-  constexpr int U = static_cast<int>(kTileElems / (kThreads * VE));
+  using Vec = typename In<InT>::Vec;
+  constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
 
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    int lo = 0, hi = a.nseg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.segs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
-    }
-    const Seg sg = a.segs[lo];
+    const Seg sg = a.segs[find_seg(a.segs, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
 
-    // First offset j (0 <= j < VE) at which every stream is 16-byte aligned.
+    // First offset j (0 <= j < 4) at which every stream is slot-aligned.
     int j0 = -1;
     for (int j = 0; j < VE && j0 < 0; ++j) {
       bool ok = true;
       if (!sg.pad)
         for (int r = 0; r < rr; ++r)
-          ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT), 16);
+          ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT),
+                             VE * sizeof(InT));
       const uint64_t p4 = static_cast<uint64_t>(sg.part + j) * 4;
       if constexpr (kFused) {
         ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.m) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.v) + p4, 16);
-        if (a.pbf16)
-          ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) + p4 / 2, VE * 2);
+        if (a.pbf16) ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) + p4 / 2, 8);
         if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, 16);
       } else {
         ok = ok && aligned(a.out[sg.dst] + p4, 16);
@@ -235,61 +341,66 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const RedArgs a) {
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
 
+    // Per-tile stream bases: element rel0 of the segment in every stream.
+    const uint64_t in_off = static_cast<uint64_t>(sg.flat + rel0) * sizeof(InT);
+    const uint64_t p4 = static_cast<uint64_t>(sg.part + rel0) * 4;
+    uint64_t b_master = 0, b_m = 0, b_v = 0, b_pb = 0, b_go = 0, b_out = 0;
+    if constexpr (kFused) {
+      b_master = reinterpret_cast<uint64_t>(a.master) + p4;
+      b_m = reinterpret_cast<uint64_t>(a.m) + p4;
+      b_v = reinterpret_cast<uint64_t>(a.v) + p4;
+      b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + p4 / 2 : 0;
+      b_go = a.gout ? reinterpret_cast<uint64_t>(a.gout) + p4 : 0;
+    } else {
+      b_out = a.out[sg.dst] + p4;
+    }
+
+    // Issue every load of the tile's slots first.
+    Vec w[kSlots][kRL];
+    f32x4 s0[kSlots], s1[kSlots], s2[kSlots];
+    bool full[kSlots];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
-      if (rel >= sg.numel || rel + VE <= 0) continue;
-      if (vec && rel >= 0 && rel + VE <= sg.numel) {
-        float g[VE];
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
+      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if (full[u]) {
+        if constexpr (R > 0) {
+          if (!sg.pad) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+          }
+        }
+        if constexpr (kFused) {
+          s0[u] = ld_tile<f32x4>(b_master, slot * 16);
+          s1[u] = ld_tile<f32x4>(b_m, slot * 16);
+          s2[u] = ld_tile<f32x4>(b_v, slot * 16);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
+      if (full[u]) {
+        float g[4];
         if (sg.pad) {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) g[e] = 0.0f;
+          for (int e = 0; e < 4; ++e) g[e] = 0.0f;
+        } else if constexpr (R > 0) {
+          reduce_slot<InT, R, kDiv>(a, w[u], g);
         } else {
-          reduce_vec<InT, R, kDiv>(a, rr, sg.flat + rel, g);
+          reduce_slot_rt<InT, kDiv>(a, rr, sg.flat + rel, g);
         }
-        const int64_t j = sg.part + rel;
         if constexpr (!kFused) {
-          float* o = reinterpret_cast<float*>(a.out[sg.dst]) + j;
-#pragma unroll
-          for (int q = 0; q < VE / 4; ++q)
-            st_stream<f32x4>(o + 4 * q, f32x4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]});
+          st_tile<f32x4>(b_out, slot * 16, f32x4{g[0], g[1], g[2], g[3]});
         } else {
-          float th[VE], mm[VE], vv[VE];
-#pragma unroll
-          for (int q = 0; q < VE / 4; ++q) {
-            const f32x4 a0 = ld_stream<f32x4>(a.master + j + 4 * q);
-            const f32x4 a1 = ld_stream<f32x4>(a.m + j + 4 * q);
-            const f32x4 a2 = ld_stream<f32x4>(a.v + j + 4 * q);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              th[4 * q + i] = a0[i];
-              mm[4 * q + i] = a1[i];
-              vv[4 * q + i] = a2[i];
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < VE; ++e) adam_elem(a.ac, g[e], th[e], mm[e], vv[e]);
-#pragma unroll
-          for (int q = 0; q < VE / 4; ++q) {
-            st_stream<f32x4>(a.master + j + 4 * q, f32x4{th[4 * q], th[4 * q + 1], th[4 * q + 2], th[4 * q + 3]});
-            st_stream<f32x4>(a.m + j + 4 * q, f32x4{mm[4 * q], mm[4 * q + 1], mm[4 * q + 2], mm[4 * q + 3]});
-            st_stream<f32x4>(a.v + j + 4 * q, f32x4{vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]});
-            if (a.gout)
-              st_stream<f32x4>(a.gout + j + 4 * q, f32x4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]});
-          }
-          if (a.pbf16) {
-            uint32_t h[VE];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) h[e] = bf16_rne(th[e]);
-            if constexpr (VE == 8) {
-              st_stream<u32x4>(a.pbf16 + j, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
-            } else {
-              st_stream<u32x2>(a.pbf16 + j, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-            }
-          }
+          adam_slot(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
+                    slot * 16, slot * 8);
         }
-      } else {
+      } else if (rel < sg.numel && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
         for (int64_t e = e0; e < e1; ++e) {
@@ -327,41 +438,45 @@ struct AdamArgs {
 // Contiguous partition; kVec: every pointer 16-byte aligned (bf16 8-byte).
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
-  constexpr int64_t VE = 4;
   const int64_t ntiles = (a.n + kTileElems - 1) / kTileElems;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const uint64_t t4 = static_cast<uint64_t>(t) * kTileElems * 4;
+    const uint64_t b_g = reinterpret_cast<uint64_t>(a.grad) + t4;
+    const uint64_t b_master = reinterpret_cast<uint64_t>(a.master) + t4;
+    const uint64_t b_m = reinterpret_cast<uint64_t>(a.m) + t4;
+    const uint64_t b_v = reinterpret_cast<uint64_t>(a.v) + t4;
+    const uint64_t b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + t4 / 2 : 0;
+    f32x4 g[kSlots], th[kSlots], mm[kSlots], vv[kSlots];
+    bool full[kSlots];
 #pragma unroll
-    for (int u = 0; u < static_cast<int>(kTileElems / (kThreads * VE)); ++u) {
-      const int64_t j = t * kTileElems + (u * kThreads + threadIdx.x) * VE;
-      if (j >= a.n) continue;
-      if (kVec && j + VE <= a.n) {
-        const f32x4 g = ld_stream<f32x4>(a.grad + j);
-        f32x4 th = ld_stream<f32x4>(a.master + j);
-        f32x4 mm = ld_stream<f32x4>(a.m + j);
-        f32x4 vv = ld_stream<f32x4>(a.v + j);
-        float t4[4], m4[4], v4[4];
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t j = t * kTileElems + static_cast<int64_t>(slot) * VE;
+      full[u] = kVec && j + VE <= a.n;
+      if (full[u]) {
+        g[u] = ld_tile<f32x4>(b_g, slot * 16);
+        th[u] = ld_tile<f32x4>(b_master, slot * 16);
+        mm[u] = ld_tile<f32x4>(b_m, slot * 16);
+        vv[u] = ld_tile<f32x4>(b_v, slot * 16);
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t4[e] = th[e];
-          m4[e] = mm[e];
-          v4[e] = vv[e];
-          adam_elem(a.ac, g[e], t4[e], m4[e], v4[e]);
-        }
-        st_stream<f32x4>(a.master + j, f32x4{t4[0], t4[1], t4[2], t4[3]});
-        st_stream<f32x4>(a.m + j, f32x4{m4[0], m4[1], m4[2], m4[3]});
-        st_stream<f32x4>(a.v + j, f32x4{v4[0], v4[1], v4[2], v4[3]});
-        if (a.pbf16)
-          st_stream<u32x2>(a.pbf16 + j, u32x2{bf16_rne(t4[0]) | (bf16_rne(t4[1]) << 16),
-                                              bf16_rne(t4[2]) | (bf16_rne(t4[3]) << 16)});
-      } else {
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t j = t * kTileElems + static_cast<int64_t>(slot) * VE;
+      if (full[u]) {
+        const float gg[4] = {g[u][0], g[u][1], g[u][2], g[u][3]};
+        adam_slot(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
+                  slot * 16, slot * 8);
+      } else if (j < a.n) {
         const int64_t e1 = j + VE < a.n ? j + VE : a.n;
         for (int64_t e = j; e < e1; ++e) {
-          float th = a.master[e], mm = a.m[e], vv = a.v[e];
-          adam_elem(a.ac, a.grad[e], th, mm, vv);
-          a.master[e] = th;
-          a.m[e] = mm;
-          a.v[e] = vv;
-          if (a.pbf16) a.pbf16[e] = static_cast<uint16_t>(bf16_rne(th));
+          float t1 = a.master[e], m1 = a.m[e], v1 = a.v[e];
+          adam_elem(a.ac, a.grad[e], t1, m1, v1);
+          a.master[e] = t1;
+          a.m[e] = m1;
+          a.v[e] = v1;
+          if (a.pbf16) a.pbf16[e] = static_cast<uint16_t>(bf16_rne(t1));
         }
       }
     }
@@ -386,8 +501,7 @@ struct IpgArgs {
 
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
-  constexpr int VE = In<InT>::VE;
-  constexpr int U = static_cast<int>(kTileElems / (kThreads * VE));
+  using Vec = typename In<InT>::Vec;
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
     int s = 0;
     while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
@@ -396,31 +510,38 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
     const uint64_t mg = reinterpret_cast<uint64_t>(a.main_grad);
     int j0 = -1;
     for (int j = 0; j < VE && j0 < 0; ++j)
-      if (aligned(sg.src + j * sizeof(InT), 16) &&
+      if (aligned(sg.src + j * sizeof(InT), VE * sizeof(InT)) &&
           aligned(mg + static_cast<uint64_t>(sg.dst + j) * 4, 16))
         j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    Vec x[kSlots];
+    f32x4 cur[kSlots];
+    bool full[kSlots];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
-      if (rel >= sg.numel || rel + VE <= 0) continue;
-      if (vec && rel >= 0 && rel + VE <= sg.numel) {
-        float x[VE];
-        In<InT>::unpack(ld_stream<u32x4>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT))), x);
-        float* o = a.main_grad + sg.dst + rel;
+      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if (full[u]) {
+        x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+        cur[u] = ld_stream<f32x4>(a.main_grad + sg.dst + rel);
+      }
+    }
 #pragma unroll
-        for (int q = 0; q < VE / 4; ++q) {
-          const f32x4 cur = ld_stream<f32x4>(o + 4 * q);
-          st_stream<f32x4>(o + 4 * q, f32x4{cur[0] + x[4 * q], cur[1] + x[4 * q + 1],
-                                            cur[2] + x[4 * q + 2], cur[3] + x[4 * q + 3]});
-        }
-      } else {
+    for (int u = 0; u < kSlots; ++u) {
+      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
+      if (full[u]) {
+        float g[4];
+        In<InT>::unpack(x[u], g);
+        st_stream<f32x4>(a.main_grad + sg.dst + rel,
+                         f32x4{cur[u][0] + g[0], cur[u][1] + g[1], cur[u][2] + g[2],
+                               cur[u][3] + g[3]});
+      } else if (rel < sg.numel && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
         for (int64_t e = e0; e < e1; ++e) {
-          const float x = In<InT>::widen(*reinterpret_cast<const InT*>(sg.src + e * sizeof(InT)));
-          a.main_grad[sg.dst + e] = a.main_grad[sg.dst + e] + x;
+          const float v = In<InT>::widen(*reinterpret_cast<const InT*>(sg.src + e * sizeof(InT)));
+          a.main_grad[sg.dst + e] = a.main_grad[sg.dst + e] + v;
         }
       }
     }
@@ -438,15 +559,8 @@ struct CopyArgs {
 };
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
-  constexpr int VE = 4;
-  constexpr int U = static_cast<int>(kTileElems / (kThreads * VE));
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    int lo = 0, hi = a.nseg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.segs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
-    }
-    const Seg sg = a.segs[lo];
+    const Seg sg = a.segs[find_seg(a.segs, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
     const float* s = a.src + sg.flat;
     float* d = a.dst + sg.part;
@@ -457,13 +571,20 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
         j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    f32x4 x[kSlots];
+    bool full[kSlots];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
-      if (rel >= sg.numel || rel + VE <= 0) continue;
-      if (vec && rel >= 0 && rel + VE <= sg.numel) {
-        st_stream<f32x4>(d + rel, ld_stream<f32x4>(s + rel));
-      } else {
+      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
+      if (full[u]) {
+        st_stream<f32x4>(d + rel, x[u]);
+      } else if (rel < sg.numel && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
         for (int64_t e = e0; e < e1; ++e) d[e] = s[e];
@@ -483,8 +604,6 @@ struct RingArgs {
 };
 
 __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
-  constexpr int VE = 4;
-  constexpr int U = static_cast<int>(kTileElems / (kThreads * VE));
   const int64_t total = a.tiles_per_rank * a.n;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
@@ -501,15 +620,24 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
         j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    f32x4 x[kSlots], y[kSlots];
+    bool full[kSlots];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
-      if (rel >= a.chunk || rel + VE <= 0) continue;
-      if (vec && rel >= 0 && rel + VE <= a.chunk) {
-        const f32x4 x = ld_stream<f32x4>(s + rel);
-        const f32x4 y = ld_stream<f32x4>(d + rel);
-        st_stream<f32x4>(d + rel, f32x4{y[0] + x[0], y[1] + x[1], y[2] + x[2], y[3] + x[3]});
-      } else {
+      full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
+      if (full[u]) {
+        x[u] = ld_stream<f32x4>(s + rel);
+        y[u] = ld_stream<f32x4>(d + rel);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
+      if (full[u]) {
+        st_stream<f32x4>(d + rel, f32x4{y[u][0] + x[u][0], y[u][1] + x[u][1],
+                                        y[u][2] + x[u][2], y[u][3] + x[u][3]});
+      } else if (rel < a.chunk && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < a.chunk ? rel + VE : a.chunk;
         for (int64_t e = e0; e < e1; ++e) d[e] = d[e] + s[e];
@@ -521,8 +649,8 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
 // ================================================================= host ===
 
 int64_t tiles_for(int64_t numel) {
-  // +7: a segment whose start is not group-aligned spans one extra group.
-  return (numel + 7 + kTileElems - 1) / kTileElems;
+  // + VE - 1: a segment whose start is not slot-aligned spans one more slot.
+  return (numel + VE - 1 + kTileElems - 1) / kTileElems;
 }
 
 // Launch tables derived from a plan: the host segment list (pure host data,
@@ -585,8 +713,11 @@ zr_status device_info(int* dev, int* cus) {
   return ZR_OK;
 }
 
+// One workgroup per tile (ZR_GRID_PER_CU == 0), else a capped grid-stride
+// grid.  Kernels loop over tiles either way, so any grid size is correct.
 unsigned grid_for(int64_t tiles, int cus) {
-  const int64_t cap = static_cast<int64_t>(cus) * 8;
+  const int64_t cap = ZR_GRID_PER_CU > 0 ? static_cast<int64_t>(cus) * ZR_GRID_PER_CU
+                                         : int64_t(1) << 30;
   return static_cast<unsigned>(std::max<int64_t>(1, std::min(tiles, cap)));
 }
 
