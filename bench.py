@@ -18,6 +18,7 @@ partition.  Other workloads (``--workload``) are for characterisation.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -48,33 +49,35 @@ def traffic_for(kernel_key):
 
 
 class Timer:
-    """Counts launches per kernel label; when a step launches more than one
-    kind of kernel it also brackets every launch with HIP events (on the
-    launch stream, torch's current stream) to split the time per kernel."""
+    """Counts launches per kernel label.  With ``only`` set, launches of other
+    labels are skipped, so one kernel of a multi-kernel step can be timed
+    back to back on its own."""
 
-    def __init__(self, torch, per_launch):
-        self.torch = torch
-        self.per_launch = per_launch
-        self.ev = []
+    def __init__(self, only=None):
+        self.only = only
         self.count = {}
 
     def launch(self, fn, label):
-        self.count[label] = self.count.get(label, 0) + 1
-        if not self.per_launch:
-            fn()
+        if self.only is not None and label != self.only:
             return
-        a = self.torch.cuda.Event(enable_timing=True)
-        b = self.torch.cuda.Event(enable_timing=True)
-        a.record()
+        self.count[label] = self.count.get(label, 0) + 1
         fn()
-        b.record()
-        self.ev.append((a, b, label))
 
-    def per_label_ms(self):
-        out = {}
-        for a, b, label in self.ev:
-            out.setdefault(label, []).append(a.elapsed_time(b))
-        return out
+
+def timed_region(torch, step, first, steps, only=None):
+    """Run ``steps`` steps between two HIP events on the launch stream (torch's
+    current stream); returns (wall seconds, event seconds, launch counts)."""
+    timer = Timer(only)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(first + i, timer)
+    ev1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, 1e-3 * ev0.elapsed_time(ev1), timer.count
 
 
 # --------------------------------------------------------------- workloads
@@ -113,6 +116,281 @@ def setup_gpt2(torch, zr, workloads):
         return cpu_oracle_fused(torch, workloads, plan, name, w, reps, states[0]["master"], P, R)
 
     return step, bytes_per_step, P, cfg, launch_bytes, "fused", cpu_leg
+
+
+def setup_gpt2_unfused(torch, zr, workloads, copy_only=False):
+    """The same rank shares as the default, as separate launches: the
+    reduce-scatter with its fused store into the partition (a3+a4), then the
+    standalone partition Adam (a5); or only the standalone copy of a reduced
+    bucket-layout buffer into the partition (a4)."""
+    name = "gpt2-small"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    T, L, P, D = zr.zr_plan_group_info(plan, 0)
+    R = w.groups[0][0]
+    if copy_only:
+        src = workloads.device_normal(workloads.seed_for(name, 0, 7), T, w.grad_sigma, "cuda")
+        parts = [torch.empty(P, device="cuda") for _ in range(R)]
+
+        def step(i, timer):
+            k = i % R
+            timer.launch(lambda: zr.zr_copy_grads_in_partition(plan, 0, 0, k, src, parts[k]),
+                         "copy")
+
+        cfg = {"workload": name + "-copy-in-partition", "partition_elems": P,
+               "bytes_per_step": 8 * P, "share": "one rank's slices of the one bucket"}
+        return step, 8 * P, P, cfg, {"copy": 8 * P}, "copy", None
+    reps = [workloads.device_normal(workloads.seed_for(name, r), T, w.grad_sigma, "cuda", "bf16")
+            for r in range(R)]
+    states = []
+    for k in range(R):
+        master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                         w.master_sigma, "cuda")
+        states.append(dict(master=master, m=torch.zeros_like(master),
+                           v=torch.zeros_like(master), g=torch.empty_like(master),
+                           pbf16=torch.empty(P, dtype=torch.bfloat16, device="cuda")))
+    rb, ab = (R * 2 + 4) * P, 30 * P
+
+    def step(i, timer):
+        k = i % R
+        s = states[k]
+        timer.launch(lambda: zr.zr_reduce_scatter_local(plan, 0, -1, k, reps, [s["g"]]), "reduce")
+        timer.launch(lambda: zr.zr_adam_partition(s["g"], s["master"], s["m"], s["v"], s["pbf16"],
+                                                  step=i // R + 1, **HP), "adam")
+
+    cfg = {"workload": name + "-unfused", "replicas": R, "grad_dtype": "bf16",
+           "partition_elems": P, "bytes_per_step": rb + ab,
+           "share": "one rank's partition per step: reduce-scatter, then Adam"}
+    return step, rb + ab, P, cfg, {"reduce": rb, "adam": ab}, "reduce", None
+
+
+def setup_gpt2_allgather(torch, zr, workloads):
+    """Parameter all-gather after the update: one rank rebuilds the full bf16
+    parameter vector (124,439,808 elements) from the 8 updated partitions."""
+    name = "gpt2-small"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    T, L, P, D = zr.zr_plan_group_info(plan, 0)
+    R = w.groups[0][0]
+    parts = [workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                     w.master_sigma, "cuda", "bf16") for k in range(R)]
+    outs = [torch.empty(T, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    b = 4 * T
+
+    def step(i, timer):
+        timer.launch(lambda: zr.zr_all_gather_params(plan, 0, parts, outs[i % 2]), "allgather")
+
+    cfg = {"workload": name + "-allgather", "total_elems": T, "replicas": R,
+           "bytes_per_step": b, "share": "one rank's full bf16 parameter vector"}
+    return step, b, T, cfg, {"allgather": b}, "allgather", None
+
+
+def setup_gpt2_dp(torch, zr, workloads):
+    """Plain data parallelism on one GPU's share, the baseline the method
+    replaces: the all-reduce average of the whole flat vector (every
+    partition of the reduce-scatter, written contiguously), then Adam over
+    every parameter (optimizer state not partitioned)."""
+    name = "gpt2-small"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    T, L, P, D = zr.zr_plan_group_info(plan, 0)
+    R = w.groups[0][0]
+    reps = [workloads.device_normal(workloads.seed_for(name, r), T, w.grad_sigma, "cuda", "bf16")
+            for r in range(R)]
+    g = torch.empty(L, device="cuda")
+    parts = [g[k * P:(k + 1) * P] for k in range(R)]
+    master = workloads.device_normal(workloads.seed_for(name, 0, master=True), L, w.master_sigma,
+                                     "cuda")
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    pb = torch.empty(L, dtype=torch.bfloat16, device="cuda")
+    rb, ab = (R * 2 + 4) * L, 30 * L
+
+    def step(i, timer):
+        timer.launch(lambda: zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, parts), "allreduce")
+        timer.launch(lambda: zr.zr_adam_partition(g, master, m, v, pb, step=i + 1, **HP), "adam")
+
+    cfg = {"workload": name + "-dp-baseline", "replicas": R, "total_elems": T,
+           "bytes_per_step": rb + ab,
+           "share": "plain DP: full averaged gradient and Adam on every parameter"}
+    return step, rb + ab, L, cfg, {"allreduce": rb, "adam": ab}, "adam", None
+
+
+def setup_ring_allreduce(torch, zr, workloads):
+    """Ring all-reduce emulation: the 7 reduce-scatter steps then the 7
+    all-gather steps, all 8 ranks resident (the all-reduce baseline)."""
+    c = workloads.RING_1GIB
+    N, M = c["ranks"], c["elems_per_rank"]
+    C = M // N
+    bufs = [workloads.device_normal(workloads.seed_for("ring-1gib", r), M, c["sigma"], "cuda")
+            for r in range(N)]
+    rs, ag = 12 * C * N, 8 * C * N
+
+    def step(i, timer):
+        for s in range(N - 1):
+            timer.launch(lambda: zr.zr_ring_rs_step(bufs, C, s), "ring_rs")
+        for s in range(N - 1):
+            timer.launch(lambda: zr.zr_ring_ag_step(bufs, C, s), "ring_ag")
+
+    b = (N - 1) * (rs + ag)
+    cfg = {"workload": "ring-1gib-allreduce", "ranks": N, "chunk_elems": C,
+           "bytes_per_step": b}
+    return step, b, M * N, cfg, {"ring_rs": rs, "ring_ag": ag}, "ring_rs", None
+
+
+def run_overlap(torch, zr, workloads, args):
+    """Overlapped bucketed reduction behind a simulated backward, for one rank.
+
+    The plan is built over the Llama-3-8B list in gradient-ready order (last
+    layer first).  Stream A runs the backward stand-in: for every param a
+    weight-gradient GEMM (dY^T X over 2048 tokens, bf16, torch matmul) and
+    the IPG fill of that gradient into this rank's full fp32 main_grad.  As
+    soon as a bucket is complete its fused reduce-scatter + Adam for this
+    rank's partition is launched on stream B after an event from stream A;
+    the other 7 replicas' windows are resident.  Backward-only, reduce-only
+    and serial times are taken on one stream; the overlapped run uses two.
+    Checks that the overlapped result equals the serial one bit for bit."""
+    name = "llama3-8b"
+    w = workloads.get(name)
+    order = list(range(len(w.numels)))[::-1]
+    numels = [w.numels[p] for p in order]
+    shapes = [w.shapes[p] for p in order]
+    R, k, tok = 8, 0, args.tokens
+    dev = "cuda"
+    hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime torch already holds
+    created = []
+
+    def new_stream():
+        """A default-priority, non-blocking HIP stream created through the
+        runtime torch holds (no torch stream pool), destroyed after each
+        configuration."""
+        h = ctypes.c_void_p()
+        err = hip.hipStreamCreateWithFlags(ctypes.byref(h), ctypes.c_uint(1))
+        if err != 0:
+            raise RuntimeError(f"stream creation failed with HIP error {err}")
+        created.append(h)
+        return torch.cuda.ExternalStream(h.value)
+
+    def destroy_streams():
+        torch.cuda.synchronize()
+        while created:
+            hip.hipStreamDestroy(created.pop())
+
+    o_max = max(s[0] for s in shapes if len(s) == 2)
+    # Contiguous operands only (one activation matrix per input width).
+    X = {i: (torch.randn(tok, i, device=dev) * 0.1).to(torch.bfloat16)
+         for i in sorted({s[-1] for s in shapes})}
+    dYt = (torch.randn(o_max, tok, device=dev) * 0.1).to(torch.bfloat16)
+    results = {}
+    ref_master = None
+    s_full = torch.cuda.current_stream()      # serial reference on every CU
+    for B in args.buckets:
+        sa, sb = new_stream(), new_stream()
+        plan = zr.zr_plan_buckets(numels, [0] * len(numels), [(R, 1)], B)
+        T, L, P, D = zr.zr_plan_group_info(plan, 0)
+        nb = zr.zr_plan_num_buckets(plan)
+        lo = k * P
+        mg = torch.empty(T, device=dev)
+        others = [workloads.device_normal(workloads.seed_for(name, r, 7), P, 2 * w.grad_sigma, dev)
+                  for r in range(1, R)]
+        reps = [(mg, 0)] + [(x, lo) for x in others]
+        master0 = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                          w.master_sigma, dev)
+        state = {}
+        pos, ends = 0, []
+        for ne in numels:
+            pos += ne
+            ends.append(pos)
+
+        def reset():
+            mg.zero_()
+            state["master"] = master0.clone()
+            state["m"] = torch.zeros_like(master0)
+            state["v"] = torch.zeros_like(master0)
+            state["pb"] = torch.empty(P, dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+
+        def reduce_bucket(b):
+            zr.zr_reduce_scatter_adam(plan, 0, b, k, reps, state["master"], state["m"],
+                                      state["v"], state["pb"], None, **HP)
+
+        def backward(on_bucket):
+            done = 0
+            for p, (ne, shp) in enumerate(zip(numels, shapes)):
+                if len(shp) == 2:
+                    g = torch.matmul(dYt[:shp[0]], X[shp[1]]).view(-1)
+                else:
+                    g = X[shp[0]][0].clone()
+                zr.zr_ipg_accumulate(plan, [p], [g], mg, window_base=0)
+                while done < nb and ((done + 1) * B <= ends[p] or ends[p] == T):
+                    on_bucket(done)
+                    done += 1
+
+        def timed(fn):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+
+        def run_serial():
+            with torch.cuda.stream(s_full):
+                backward(lambda b: None)
+                for b in range(nb):
+                    reduce_bucket(b)
+
+        def run_overlap_once():
+            def on_bucket(b):
+                ev = torch.cuda.Event()
+                ev.record(sa)
+                sb.wait_event(ev)
+                with torch.cuda.stream(sb):
+                    reduce_bucket(b)
+            with torch.cuda.stream(sa):
+                backward(on_bucket)
+            sa.wait_stream(sb)
+
+        def run_backward():
+            with torch.cuda.stream(s_full):
+                backward(lambda b: None)
+
+        def run_reduce():
+            with torch.cuda.stream(s_full):
+                for b in range(nb):
+                    reduce_bucket(b)
+
+        reset(); run_serial(); torch.cuda.synchronize()       # warm-up
+        reset(); t_bwd = timed(run_backward)
+        t_red = timed(run_reduce)
+        reset(); t_ser = timed(run_serial)
+        serial_master = state["master"].clone()
+        reset(); run_overlap_once(); torch.cuda.synchronize()
+        reset(); t_ovl = timed(run_overlap_once)
+        same = bool(torch.equal(serial_master.view(torch.int32), state["master"].view(torch.int32)))
+        if ref_master is None:
+            ref_master = serial_master
+        same_across_b = bool(torch.equal(ref_master.view(torch.int32),
+                                         serial_master.view(torch.int32)))
+        results[f"B={B}"] = {"reduce_bucket_size": B,
+                           "buckets": nb, "t_backward_ms": 1e3 * t_bwd,
+                           "t_reduce_ms": 1e3 * t_red, "t_serial_ms": 1e3 * t_ser,
+                           "t_overlap_ms": 1e3 * t_ovl,
+                           "hidden_fraction": max(0.0, (t_ser - t_ovl) / t_red),
+                           "overlap_bitwise_equal_serial": same,
+                           "equal_across_bucket_sizes": same_across_b}
+        del mg, others, reps, master0, state
+        destroy_streams()
+        torch.cuda.empty_cache()
+    ok = all(r["overlap_bitwise_equal_serial"] and r["equal_across_bucket_sizes"]
+             for r in results.values())
+    out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "data": "synthetic",
+           "config": {"workload": "llama3-8b-overlap", "rank": k, "tokens": tok,
+                      "ready_order": "last layer first"},
+           "overlap": results, "parity_ok": ok,
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(out), flush=True)
+    if not ok:
+        sys.exit(1)
 
 
 def setup_llama(torch, zr, workloads, ipg=False):
@@ -269,9 +547,16 @@ def main():
     ap.add_argument("--steps", type=int, default=800)
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--workload", default="gpt2-small",
-                    choices=["gpt2-small", "llama3-8b", "llama3-8b-ipg", "moe-16l",
-                             "ring-1gib", "copy"])
+                    choices=["gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
+                             "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
+                             "llama3-8b-overlap",
+                             "llama3-8b", "llama3-8b-ipg", "moe-16l", "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--buckets", type=lambda t: [int(float(x)) for x in t.split(",")],
+                    default=[int(5e7), int(5e8)],
+                    help="reduce_bucket_size values for --workload llama3-8b-overlap")
+    ap.add_argument("--tokens", type=int, default=2048,
+                    help="tokens of the backward GEMM stand-in (llama3-8b-overlap)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -284,40 +569,39 @@ def main():
     from zero_partition_aware_amd import workloads, zr
 
     torch.cuda.set_device(0)
+    if args.workload == "llama3-8b-overlap":
+        run_overlap(torch, zr, workloads, args)
+        return
     setup = {"gpt2-small": setup_gpt2, "llama3-8b": setup_llama,
+             "gpt2-small-unfused": setup_gpt2_unfused,
+             "gpt2-small-allgather": setup_gpt2_allgather,
+             "gpt2-small-dp": setup_gpt2_dp,
+             "ring-1gib-allreduce": setup_ring_allreduce,
+             "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
              "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
              "ring-1gib": setup_ring, "copy": setup_copy}[args.workload]
     step, bytes_per_step, elems_per_step, cfg, launch_bytes, dominant, cpu_leg = \
         setup(torch, zr, workloads)
     torch.cuda.synchronize()
 
-    per_launch = len(launch_bytes) > 1
-    warm = Timer(torch, per_launch)
     for i in range(args.warmup):
-        step(i, warm)
+        step(i, Timer())
     torch.cuda.synchronize()
 
-    timer = Timer(torch, per_launch)
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    region0.record()
-    for i in range(args.steps):
-        step(args.warmup + i, timer)
-    region1.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    region_s = 1e-3 * region0.elapsed_time(region1)
-
-    if per_launch:
-        ms = timer.per_label_ms()
-        per_label_s = {k: (len(v), 1e-3 * sum(v) / len(v)) for k, v in ms.items()}
+    # The whole step: value and ms_per_step.
+    elapsed, region_s, counts = timed_region(torch, step, args.warmup, args.steps)
+    # Average launch duration of each kernel: the event-timed region divided by
+    # its launches.  When a step launches more than one kind of kernel, each
+    # kind is also run back to back on its own (same steps, other launches
+    # skipped), so no event ever sits between two different kernels.
+    per_label_s = {}
+    if len(counts) == 1:
+        (label, n), = counts.items()
+        per_label_s[label] = (n, region_s / n)
     else:
-        # One kernel per step: its average launch duration is the event-timed
-        # region divided by the launches in it (gaps between launches count).
-        (label, n), = timer.count.items()
-        per_label_s = {label: (n, region_s / n)}
+        for label in counts:
+            _, r_s, c = timed_region(torch, step, args.warmup, args.steps, only=label)
+            per_label_s[label] = (c[label], r_s / c[label])
     launches = {k: {"count": n, "avg_us": 1e6 * t,
                     "achieved_GBps": launch_bytes[k] / t / 1e9}
                 for k, (n, t) in per_label_s.items()}

@@ -153,6 +153,13 @@ zr_status zr_plan_param_partitions(const zr_plan* plan, int64_t p,
 zr_status zr_plan_grad_start_offset(const zr_plan* plan, int64_t p, int32_t k,
                                     int64_t* out);
 
+/* The buckets param p feeds: [*first, *last] (a param split at a bucket
+ * border feeds several).  A bucket is complete once every param feeding it
+ * has been accumulated -- the trigger of its reduction ([ZeRO-RS blog] §四:
+ * a full bucket starts average_tensor). */
+zr_status zr_plan_param_buckets(const zr_plan* plan, int64_t p, int64_t* first,
+                                int64_t* last);
+
 /* The merged slices of one bucket (bucket >= 0) or of all buckets
  * (bucket == -1), in bucket order.  *s points into the plan. */
 zr_status zr_plan_slices(const zr_plan* plan, int64_t bucket,
@@ -245,6 +252,31 @@ zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
  * element-wise over the chunk.  After steps 0..n_ranks-2, rank k's chunk k
  * holds the sum over ranks in ring order k+1, ..., k.  0 <= step <= n-2. */
 zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
+                          int64_t chunk_numel, int32_t step,
+                          hipStream_t stream);
+
+/* zr_all_gather_params -- rebuild the full flat vector of a group from its
+ * R_g partitions after the partition update ([Megatron DP] "通信模式": the
+ * all-gather that stitches the updated 1/DP slices back into full weights for
+ * the next forward; [Collectives] AllGather definition):
+ *   out[f - out_base] = parts[f / P_g][f % P_g]
+ * for flat f in [out_base, out_base + out_len), which must lie inside the
+ * group's real elements [0, T_g) (padding is not a parameter).
+ *   parts[R_g]  host array of device partition pointers (P_g elements each;
+ *               only the partitions the window touches are read).
+ *   dtype       ZR_BF16 (the 16-bit params) or ZR_FP32 (e.g. masters).
+ * A pure copy: bit-exact. */
+zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
+                               const void* const* parts, zr_dtype dtype,
+                               void* out, int64_t out_base, int64_t out_len,
+                               hipStream_t stream);
+
+/* zr_ring_ag_step -- one step of the ring all-gather phase with every card's
+ * buffer resident here ([Megatron DP] "深入：all-reduce 底层算法（NCCL）", second
+ * phase).  For every rank k: buf_k[c] = buf_{k-1}[c], c = (k - step - 1) mod
+ * n_ranks.  After the n-1 reduce-scatter steps, steps 0..n_ranks-2 of this
+ * phase leave every rank holding every reduced chunk (ring all-reduce). */
+zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
                           int64_t chunk_numel, int32_t step,
                           hipStream_t stream);
 

@@ -93,3 +93,32 @@ def test_byte_table():
     assert per_card_bytes_per_param("zero3", 8) == 2
     assert per_card_bytes_per_param("zero1", 8) == Fraction(11, 2)
     assert per_card_bytes_per_param("zero1.5", 8) == Fraction(2) + Fraction(14, 8)
+
+
+def test_all_gather_is_concatenation_by_brute_force():
+    from oracle.allgather import all_gather_oracle, all_gather_window_oracle
+    rng = np.random.default_rng(3)
+    for R, P, T in [(4, 5, 18), (2, 3, 6), (8, 1, 5), (3, 7, 21)]:
+        parts = [rng.standard_normal(P).astype(F) for _ in range(R)]
+        full = all_gather_oracle(parts, T)
+        for f in range(T):                       # element f lives in partition f // P
+            assert full[f] == parts[f // P][f % P]
+        assert full.shape[0] == T
+        got = all_gather_window_oracle(parts, T, 2, 100)
+        assert np.array_equal(got, full[2:])
+
+
+def test_reduce_scatter_then_all_gather_is_all_reduce():
+    # All-reduce = reduce-scatter followed by all-gather: gathering the
+    # shards of the partition-aware reduction gives the all-reduce average.
+    from oracle.allgather import all_gather_oracle
+    from oracle.plan import plan_oracle
+    from oracle.reduce import allreduce_average_oracle, reduce_scatter_oracle
+    rng = np.random.default_rng(4)
+    numels = [37, 2112, 129]
+    plan = plan_oracle(numels, [0, 0, 0], [(4, 1)], 1000)
+    reps = [rng.standard_normal(2278).astype(F) for _ in range(4)]
+    shards = reduce_scatter_oracle(plan, 0, reps, False)
+    full = all_gather_oracle([shards[k] for k in range(4)], 2278)
+    ar = allreduce_average_oracle(reps, 4, False)
+    assert np.array_equal(full.view(np.uint32), ar.view(np.uint32))

@@ -97,3 +97,24 @@ def test_query_errors():
         zr.zr_plan_slices(plan, 3)
     with pytest.raises(zr.ZrError):
         zr.zr_plan_group_info(plan, 1)
+
+
+def test_param_buckets_match_list_positions():
+    rng = random.Random(7)
+    for _ in range(100):
+        n = rng.randint(1, 30)
+        numels = [rng.randint(1, 3000) for _ in range(n)]
+        pg = [rng.randrange(2) for _ in range(n)]
+        B = rng.choice([1, 100, 2999, 10 ** 6])
+        ref = plan_oracle(numels, pg, [(2, 1), (4, 2)], B)
+        plan = zr.zr_plan_buckets(numels, pg, [(2, 1), (4, 2)], B)
+        pos = 0
+        for p, ne in enumerate(numels):
+            first, last = zr.zr_plan_param_buckets(plan, p)
+            assert (first, last) == (pos // B, (pos + ne - 1) // B)
+            # every bucket in that range holds a slice of this param
+            mine = {s.bucket for s in ref.slices if s.group == pg[p] and
+                    s.flat_offset < ref.param_offset[p] + ne and
+                    s.flat_offset + s.numel > ref.param_offset[p]}
+            assert mine == set(range(first, last + 1))
+            pos += ne

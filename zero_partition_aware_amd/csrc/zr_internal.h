@@ -27,6 +27,7 @@ struct ParamInfo {
   int64_t numel = 0;
   int32_t group = 0;
   int64_t offset = 0;                 // o_p in the group's flat space
+  int64_t list_pos = 0;               // position in the list-ordered bucket space
   std::vector<int32_t> partitions;    // param_to_partition_ids
   std::vector<int64_t> start_offsets; // grad_start_offset, aligned with above
 };

@@ -40,6 +40,7 @@
 #include <set>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "zr_internal.h"
@@ -646,6 +647,107 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------- gather ---
+
+constexpr int kXMaxSegs = ZR_MAX_WORLD;
+
+struct XSeg {
+  uint64_t src;   // address of the segment's first source element
+  uint64_t dst;   // address of its first destination element
+  int64_t numel;
+  int64_t tile0;
+};
+
+struct XArgs {
+  XSeg seg[kXMaxSegs];
+  int64_t total_tiles;
+  int32_t nseg;
+};
+
+// Segmented copy driven by a table in the kernel arguments; T is uint16_t
+// (bf16 patterns) or float.  Used by the parameter all-gather.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
+  using Vec = typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type;
+  constexpr int ES = sizeof(T);
+  for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+    int s = 0;
+    while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
+    const XSeg sg = a.seg[s];
+    const int64_t lt = t - sg.tile0;
+    int j0 = -1;
+    for (int j = 0; j < VE && j0 < 0; ++j)
+      if (aligned(sg.src + j * ES, VE * ES) && aligned(sg.dst + j * ES, VE * ES)) j0 = j;
+    const bool vec = j0 >= 0;
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    const uint64_t bs = sg.src + rel0 * ES, bd = sg.dst + rel0 * ES;
+    Vec x[kSlots];
+    bool full[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
+      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if (full[u]) x[u] = ld_tile<Vec>(bs, slot * VE * ES);
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
+      if (full[u]) {
+        st_tile<Vec>(bd, slot * VE * ES, x[u]);
+      } else if (rel < sg.numel && rel + VE > 0) {
+        const int64_t e0 = rel < 0 ? 0 : rel;
+        const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
+        for (int64_t e = e0; e < e1; ++e)
+          reinterpret_cast<T*>(sg.dst)[e] = reinterpret_cast<const T*>(sg.src)[e];
+      }
+    }
+  }
+}
+
+// Ring all-gather step: rank k copies chunk (k - step - 1) mod n from rank
+// k-1's buffer into its own.
+__global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
+  const int64_t total = a.tiles_per_rank * a.n;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int k = static_cast<int>(t / a.tiles_per_rank);
+    const int64_t lt = t - static_cast<int64_t>(k) * a.tiles_per_rank;
+    int c = (k - a.step - 1) % a.n;
+    if (c < 0) c += a.n;
+    const int prev = (k == 0) ? a.n - 1 : k - 1;
+    float* d = reinterpret_cast<float*>(a.buf[k]) + static_cast<int64_t>(c) * a.chunk;
+    const float* s = reinterpret_cast<const float*>(a.buf[prev]) + static_cast<int64_t>(c) * a.chunk;
+    int j0 = -1;
+    for (int j = 0; j < VE && j0 < 0; ++j)
+      if (aligned(reinterpret_cast<uint64_t>(s + j), 16) &&
+          aligned(reinterpret_cast<uint64_t>(d + j), 16))
+        j0 = j;
+    const bool vec = j0 >= 0;
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    f32x4 x[kSlots];
+    bool full[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
+      full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
+      if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
+      if (full[u]) {
+        st_stream<f32x4>(d + rel, x[u]);
+      } else if (rel < a.chunk && rel + VE > 0) {
+        const int64_t e0 = rel < 0 ? 0 : rel;
+        const int64_t e1 = rel + VE < a.chunk ? rel + VE : a.chunk;
+        for (int64_t e = e0; e < e1; ++e) d[e] = s[e];
+      }
+    }
+  }
+}
+
 // ================================================================= host ===
 
 int64_t tiles_for(int64_t numel) {
@@ -1129,10 +1231,60 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
   }
 }
 
-extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
-                                     int64_t chunk_numel, int32_t step,
-                                     hipStream_t stream) {
+
+extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
+                                          const void* const* parts, zr_dtype dtype,
+                                          void* out, int64_t out_base, int64_t out_len,
+                                          hipStream_t stream) {
   zr::clear_error();
+  try {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
+    if (group < 0 || group >= static_cast<int32_t>(plan->groups.size()))
+      return fail(ZR_ERR_INVALID, "group index out of range");
+    if (!valid_dtype(dtype)) return fail(ZR_ERR_INVALID, "unsupported element dtype");
+    if (out_base < 0 || out_len < 0)
+      return fail(ZR_ERR_INVALID, "window base and length must be >= 0");
+    const zr::GroupInfo& gi = plan->groups[group];
+    if (out_base + out_len > gi.total)
+      return fail(ZR_ERR_INVALID, "window runs past the group's real elements");
+    if (out_len == 0) return ZR_OK;
+    const size_t es = dtype_size(dtype);
+    if (!parts) return fail(ZR_ERR_INVALID, "parts is null");
+    if (!out || !elem_aligned(out, es)) return fail(ZR_ERR_INVALID, "out is null or misaligned");
+    XArgs a;
+    std::memset(&a, 0, sizeof(a));
+    int64_t tiles = 0;
+    int n = 0;
+    for (int32_t k = 0; k < gi.world; ++k) {
+      const int64_t lo = std::max(out_base, k * gi.part);
+      const int64_t hi = std::min(out_base + out_len, (k + 1) * gi.part);
+      if (lo >= hi) continue;
+      if (!parts[k] || !elem_aligned(parts[k], es))
+        return fail(ZR_ERR_INVALID, "partition " + std::to_string(k) + " is null or misaligned");
+      XSeg& g = a.seg[n++];
+      g.src = reinterpret_cast<uint64_t>(parts[k]) + static_cast<uint64_t>(lo - k * gi.part) * es;
+      g.dst = reinterpret_cast<uint64_t>(out) + static_cast<uint64_t>(lo - out_base) * es;
+      g.numel = hi - lo;
+      g.tile0 = tiles;
+      tiles += tiles_for(g.numel);
+    }
+    a.nseg = n;
+    a.total_tiles = tiles;
+    int device = 0, cus = 1;
+    zr_status st = device_info(&device, &cus);
+    if (st != ZR_OK) return st;
+    if (dtype == ZR_BF16) gather_kernel<uint16_t><<<grid_for(tiles, cus), kThreads, 0, stream>>>(a);
+    else gather_kernel<float><<<grid_for(tiles, cus), kThreads, 0, stream>>>(a);
+    return check_launch("all_gather_params launch");
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
+
+// Shared validation of the ring steps.
+namespace {
+zr_status ring_args(float* const* rank_bufs, int32_t n_ranks, int64_t chunk_numel,
+                    int32_t step, RingArgs* a) {
   if (n_ranks < 2 || n_ranks > ZR_MAX_WORLD)
     return fail(ZR_ERR_INVALID, "n_ranks must lie in [2, ZR_MAX_WORLD]");
   if (step < 0 || step > n_ranks - 2) return fail(ZR_ERR_INVALID, "step out of range");
@@ -1149,17 +1301,40 @@ extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
         return fail(ZR_ERR_INVALID, "rank buffers overlap");
     }
   }
-  if (chunk_numel == 0) return ZR_OK;
-  int device = 0, cus = 1;
-  zr_status st = device_info(&device, &cus);
-  if (st != ZR_OK) return st;
+  std::memset(a, 0, sizeof(*a));
+  for (int k = 0; k < n_ranks; ++k) a->buf[k] = reinterpret_cast<uint64_t>(rank_bufs[k]);
+  a->chunk = chunk_numel;
+  a->tiles_per_rank = tiles_for(chunk_numel);
+  a->n = n_ranks;
+  a->step = step;
+  return ZR_OK;
+}
+}  // namespace
+
+extern "C" zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
+                                     int64_t chunk_numel, int32_t step,
+                                     hipStream_t stream) {
+  zr::clear_error();
   RingArgs a;
-  std::memset(&a, 0, sizeof(a));
-  for (int k = 0; k < n_ranks; ++k) a.buf[k] = reinterpret_cast<uint64_t>(rank_bufs[k]);
-  a.chunk = chunk_numel;
-  a.tiles_per_rank = tiles_for(chunk_numel);
-  a.n = n_ranks;
-  a.step = step;
+  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, &a);
+  if (st != ZR_OK || chunk_numel == 0) return st;
+  int device = 0, cus = 1;
+  st = device_info(&device, &cus);
+  if (st != ZR_OK) return st;
+  ring_ag_kernel<<<grid_for(a.tiles_per_rank * n_ranks, cus), kThreads, 0, stream>>>(a);
+  return check_launch("ring_ag_step launch");
+}
+
+extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
+                                     int64_t chunk_numel, int32_t step,
+                                     hipStream_t stream) {
+  zr::clear_error();
+  RingArgs a;
+  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, &a);
+  if (st != ZR_OK || chunk_numel == 0) return st;
+  int device = 0, cus = 1;
+  st = device_info(&device, &cus);
+  if (st != ZR_OK) return st;
   ring_kernel<<<grid_for(a.tiles_per_rank * n_ranks, cus), kThreads, 0, stream>>>(a);
   return check_launch("ring_rs_step launch");
 }

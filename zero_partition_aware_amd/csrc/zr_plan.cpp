@@ -91,6 +91,7 @@ zr_status build_plan(const zr_param* params, int64_t n_params,
     plan->params[p].numel = in.numel;
     plan->params[p].group = in.group;
     plan->params[p].offset = gi.total;
+    plan->params[p].list_pos = list_total;
     gi.total += in.numel;
     list_total += in.numel;
   }
@@ -270,6 +271,16 @@ extern "C" zr_status zr_plan_grad_start_offset(const zr_plan* plan, int64_t p,
       return ZR_OK;
     }
   return fail(ZR_ERR_INVALID, "param does not touch that partition");
+}
+
+extern "C" zr_status zr_plan_param_buckets(const zr_plan* plan, int64_t p,
+                                           int64_t* first, int64_t* last) {
+  if (!plan || !first || !last) return fail(ZR_ERR_INVALID, "null argument");
+  if (p < 0 || p >= static_cast<int64_t>(plan->params.size()))
+    return fail(ZR_ERR_INVALID, "param index out of range");
+  *first = plan->params[p].list_pos / plan->bucket_size;
+  *last = (plan->params[p].list_pos + plan->params[p].numel - 1) / plan->bucket_size;
+  return ZR_OK;
 }
 
 extern "C" zr_status zr_plan_slices(const zr_plan* plan, int64_t bucket,

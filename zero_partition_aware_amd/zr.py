@@ -92,6 +92,7 @@ _sigs = {
     "zr_plan_param_partitions": (c_i32, [c_vp, c_i64, _P(_P(c_i32)), _P(c_i32)]),
     "zr_plan_grad_start_offset": (c_i32, [c_vp, c_i64, c_i32, _P(c_i64)]),
     "zr_plan_slices": (c_i32, [c_vp, c_i64, _P(_P(zr_slice)), _P(c_i64)]),
+    "zr_plan_param_buckets": (c_i32, [c_vp, c_i64, _P(c_i64), _P(c_i64)]),
     "zr_ipg_accumulate": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
                                   c_i64, c_i64, c_vp]),
     "zr_reduce_scatter_local": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
@@ -104,6 +105,9 @@ _sigs = {
                                        c_i32, _P(zr_adam), c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_vp]),
     "zr_ring_rs_step": (c_i32, [_P(c_vp), c_i32, c_i64, c_i32, c_vp]),
+    "zr_ring_ag_step": (c_i32, [_P(c_vp), c_i32, c_i64, c_i32, c_vp]),
+    "zr_all_gather_params": (c_i32, [c_vp, c_i32, _P(c_vp), c_i32, c_vp, c_i64, c_i64,
+                                     c_vp]),
     "zr_last_error": (ctypes.c_char_p, []),
     "zr_version": (c_i32, []),
 }
@@ -258,6 +262,13 @@ def zr_plan_grad_start_offset(plan, p, k):
     return v.value
 
 
+def zr_plan_param_buckets(plan, p):
+    """(first, last) bucket param p feeds."""
+    a, b = c_i64(), c_i64()
+    _check(_lib.zr_plan_param_buckets(plan.handle, int(p), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
 def zr_plan_slices(plan, bucket=-1):
     """List of slice tuples (bucket, group, dst, bucket_offset, flat_offset,
     part_offset, numel)."""
@@ -336,3 +347,21 @@ def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
     arr = (c_vp * max(n, 1))(*[t.data_ptr() for t in rank_bufs])
     _check(_lib.zr_ring_rs_step(arr, n, int(chunk_numel), int(step),
                                 _stream(stream)))
+
+
+def zr_ring_ag_step(rank_bufs, chunk_numel, step, stream=None):
+    n = len(rank_bufs)
+    arr = (c_vp * max(n, 1))(*[t.data_ptr() for t in rank_bufs])
+    _check(_lib.zr_ring_ag_step(arr, n, int(chunk_numel), int(step), _stream(stream)))
+
+
+def zr_all_gather_params(plan, group, parts, out, out_base=0, out_len=None,
+                         stream=None):
+    """parts: list of R_g partition tensors (bf16 or fp32); out: tensor that
+    receives flat elements [out_base, out_base + out_len)."""
+    n = len(parts)
+    arr = (c_vp * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in parts])
+    dt = _dtype_code(out)
+    ol = out.numel() if out_len is None else int(out_len)
+    _check(_lib.zr_all_gather_params(plan.handle, int(group), arr, dt, _ptr(out),
+                                     int(out_base), ol, _stream(stream)))
