@@ -3,7 +3,8 @@
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
 // LDS staging and no MFMA.  Work is cut into tiles of kTileElems elements of
 // one "segment" (a merged slice of the plan, a param's piece of an IPG
-// window, a ring chunk); by default every workgroup takes exactly one tile, so
+// window, a ring chunk) -- 1024 elements, one 4-element slot per lane of a
+// 256-thread workgroup; by default every workgroup takes exactly one tile, so
 // the hardware dispatcher hands tiles out in address order and the set of
 // DRAM pages being touched at any moment stays compact.  A workgroup finds its
 // tile's segment by a binary search over per-segment tile offsets.
@@ -51,7 +52,7 @@ namespace {
 
 // Launch-shape constants (compile-time; the defaults are the tuned values).
 #ifndef ZR_TILE_ELEMS
-#define ZR_TILE_ELEMS 2048
+#define ZR_TILE_ELEMS 1024
 #endif
 #ifndef ZR_THREADS
 #define ZR_THREADS 256
@@ -309,8 +310,19 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
   return lo;
 }
 
+// Optional occupancy target for the reduce kernels (waves per SIMD, 0 = the
+// compiler's choice).
+#ifndef ZR_WAVES_PER_EU
+#define ZR_WAVES_PER_EU 0
+#endif
+#if ZR_WAVES_PER_EU > 0
+#define ZR_OCCUPANCY __attribute__((amdgpu_waves_per_eu(ZR_WAVES_PER_EU, 8)))
+#else
+#define ZR_OCCUPANCY
+#endif
+
 template <typename InT, int R, bool kDiv, bool kFused>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(const RedArgs a) {
+__global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const RedArgs a) {
   using Vec = typename In<InT>::Vec;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
