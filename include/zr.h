@@ -127,6 +127,9 @@ zr_status zr_plan_buckets(const zr_param* params, int64_t n_params,
                           int32_t partition_gradients, int64_t align,
                           zr_plan** out);
 
+/* Frees the plan and its device launch tables.  Freeing device memory waits
+ * for the device's outstanding work (as hipFree does), so a plan may be freed
+ * while kernels that use it are still queued; it must not be used again. */
 void zr_plan_free(zr_plan* plan);
 
 zr_status zr_plan_num_buckets(const zr_plan* plan, int64_t* out);

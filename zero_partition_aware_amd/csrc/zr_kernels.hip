@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -811,19 +812,20 @@ DevCache* cache_of(const zr_plan* plan) {
   return static_cast<DevCache*>(p->dev);
 }
 
-int g_cu_count[64] = {0};
+std::atomic<int> g_cu_count[64];  // per device, 0 until first queried
 
 zr_status device_info(int* dev, int* cus) {
   hipError_t e = hipGetDevice(dev);
   if (e != hipSuccess) return fail(ZR_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
   if (*dev < 0 || *dev >= 64) return fail(ZR_ERR_UNSUPPORTED, "device index above 63");
-  if (g_cu_count[*dev] == 0) {
-    int n = 0;
+  int n = g_cu_count[*dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, *dev);
     if (e != hipSuccess) return fail(ZR_ERR_HIP, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e));
-    g_cu_count[*dev] = n > 0 ? n : 1;
+    n = n > 0 ? n : 1;
+    g_cu_count[*dev].store(n, std::memory_order_relaxed);
   }
-  *cus = g_cu_count[*dev];
+  *cus = n;
   return ZR_OK;
 }
 
