@@ -113,7 +113,7 @@ def setup_gpt2(torch, zr, workloads):
     launch_bytes = {"fused": bytes_per_step}
 
     def cpu_leg():
-        return cpu_oracle_fused(torch, workloads, plan, name, w, reps, states[0]["master"], P, R)
+        return cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R)
 
     return step, bytes_per_step, P, cfg, launch_bytes, "fused", cpu_leg
 
@@ -513,9 +513,10 @@ def setup_copy(torch, zr, workloads):
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_oracle_fused(torch, workloads, plan, name, w, reps, master_dev, P, R):
-    """Time the CPU oracle (reduce-scatter, Adam, bf16 writeback) on rank 0's
-    whole partition, single-threaded numpy, inputs already on the host."""
+def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
+    """Time the CPU oracle (plan-driven reduce-scatter, Adam, bf16 writeback)
+    on every rank's partition of the step (the whole step of all R ranks),
+    single-threaded numpy, inputs already on the host (copies untimed)."""
     import numpy as np
     from oracle.adam import adam_oracle
     from oracle.bf16 import bf16_rne_oracle
@@ -523,19 +524,23 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, master_dev, P, R):
     from oracle.reduce import reduce_scatter_oracle
 
     ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
-    win = [r[:P].cpu().view(torch.int16).numpy().view(np.uint16) for r in reps]
-    th = master_dev.cpu().numpy()
     z = np.zeros(P, np.float32)
-    t0 = time.perf_counter()
-    g = reduce_scatter_oracle(ref, 0, win, True, dst=0)[0]
-    th1, m1, v1 = adam_oracle(g, th, z, z, step=1, **HP)
-    bf16_rne_oracle(th1)
-    dt = time.perf_counter() - t0
-    byts = (R * 2 + 26) * P
-    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "elements_per_s": P / dt, "seconds": dt,
-            "sample": f"rank 0's whole partition: {P} elements x {R} bf16 replicas "
-                      "(reduce-scatter + Adam + bf16 writeback), numpy single thread",
+    total = 0.0
+    for k in range(R):
+        win = [r[k * P:(k + 1) * P].cpu().view(torch.int16).numpy().view(np.uint16)
+               for r in reps]
+        th = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                     w.master_sigma, "cuda").cpu().numpy()
+        t0 = time.perf_counter()
+        g = reduce_scatter_oracle(ref, 0, win, True, dst=k, flat_bases=[k * P] * R)[k]
+        th1, m1, v1 = adam_oracle(g, th, z, z, step=1, **HP)
+        bf16_rne_oracle(th1)
+        total += time.perf_counter() - t0
+    byts = (R * 2 + 26) * P * R
+    return {"value": round(byts / total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "elements_per_s": round(P * R / total), "seconds": round(total, 3),
+            "sample": f"all {R} ranks' partitions of the step: {R} x {P} elements x {R} bf16 "
+                      "replicas (reduce-scatter + Adam + bf16 writeback), numpy single thread",
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
@@ -561,8 +566,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the data-parallel replicas are resident in one "
-              "GPU's HBM and the reduction is a local kernel; runs on more than one GPU "
-              "are not part of this build.", file=sys.stderr)
+              "GPU's HBM and the reduction is a local kernel, so there is no multi-GPU "
+              "run of this benchmark.", file=sys.stderr)
         sys.exit(2)
 
     import torch

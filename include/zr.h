@@ -54,7 +54,7 @@ typedef enum {
   ZR_ERR_INVALID = 1,      /* bad argument; nothing enqueued */
   ZR_ERR_OOM = 2,          /* host or device allocation failed */
   ZR_ERR_HIP = 3,          /* a HIP runtime call or launch failed */
-  ZR_ERR_UNSUPPORTED = 4   /* valid request this build does not implement */
+  ZR_ERR_UNSUPPORTED = 4   /* valid request this library does not implement */
 } zr_status;
 
 typedef enum { ZR_FP32 = 0, ZR_BF16 = 1 } zr_dtype;

@@ -15,6 +15,8 @@ import argparse
 import csv
 import json
 import os
+import shlex
+import sys
 
 from .build import source_hash
 
@@ -58,7 +60,11 @@ def main():
              "dispatches": [nf, nw],
              "fetch_scale": f_scale, "write_scale": w_scale,
              "calibration": f"copy kernel matching {args.copy_match!r}, "
-                            f"{args.copy_bytes} B read and written"}
+                            f"{args.copy_bytes} B read and written",
+             "command": "python -m zero_partition_aware_amd.traffic " +
+                        " ".join(shlex.quote(a) for a in sys.argv[1:]),
+             "counter_runs": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
+                             "-- python3 bench.py ... for the kernel and for --workload copy"}
     if args.algorithmic_bytes:
         entry["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
         entry["traffic_over_algorithmic"] = (read_b + write_b) / args.algorithmic_bytes
