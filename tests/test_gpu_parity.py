@@ -283,3 +283,32 @@ def test_invalid_call_leaves_outputs_untouched():
     assert (host_f32(out) == 7.0).all()
     zr.zr_reduce_scatter_local(plan, 0, -1, 0, reps, [out])
     assert (host_f32(out) == 1.0).all()
+
+
+@pytest.mark.parametrize("R,sp,is_bf16", [(64, 1, False), (64, 4, True), (17, 1, True), (7, 7, False)])
+def test_large_and_odd_replica_counts(R, sp, is_bf16):
+    # R = 64 is the largest world a plan accepts; 17 and 7 take the run-time
+    # replica loop; D = 64, 16, 17 and 1.
+    numels = [4096 * 3 + 11, 5, 3000]
+    ref = plan_oracle(numels, [0] * 3, [(R, sp)], 7000)
+    plan = zr.zr_plan_buckets(numels, [0] * 3, [(R, sp)], 7000)
+    info = ref.groups[0]
+    rng = np.random.default_rng(R)
+    reps = [_draw(rng, info.total, is_bf16, sigma=0.1) for _ in range(R)]
+    want = reduce_scatter_oracle(ref, 0, reps, is_bf16)
+    outs = [empty_f32(info.part_numel) for _ in range(R)]
+    zr.zr_reduce_scatter_local(plan, 0, -1, -1, [to_dev(x) for x in reps], outs)
+    for k in range(R):
+        assert_bits_equal(host_f32(outs[k]), want[k], f"R={R} dst {k}")
+    # fused on the last partition (it holds the padding)
+    k = R - 1
+    P = info.part_numel
+    th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+    th[max(0, info.total - k * P):] = 0.0
+    z = np.zeros(P, np.float32)
+    dth, dm, dv = to_dev(th), to_dev(z), to_dev(z)
+    g = empty_f32(P)
+    zr.zr_reduce_scatter_adam(plan, 0, -1, k, [to_dev(x) for x in reps], dth, dm, dv, None, g, **HP)
+    assert_bits_equal(host_f32(g), want[k], "fused grad")
+    w_th, w_m, w_v = adam_oracle(want[k], th, z, z, step=1, **HP)
+    assert_within(host_f32(dth), w_th, what="master")
