@@ -549,8 +549,8 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=800)
-    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="gpt2-small",
                     choices=["gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",

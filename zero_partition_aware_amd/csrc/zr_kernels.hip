@@ -679,40 +679,51 @@ struct XArgs {
 };
 
 // Segmented copy driven by a table in the kernel arguments; T is uint16_t
-// (bf16 patterns) or float.  Used by the parameter all-gather.
+// (bf16 patterns) or float.  Used by the parameter all-gather.  There is no
+// fp32 stream to match, so a slot is one 16-byte vector of either type
+// (8 bf16 or 4 fp32) and a tile holds kGatherTileBytes.
+constexpr int64_t kGatherTileBytes = kTileElems * 4;
+template <typename T>
+__host__ __device__ constexpr int64_t gather_tile_elems() {
+  return kGatherTileBytes / static_cast<int64_t>(sizeof(T));
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
-  using Vec = typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type;
   constexpr int ES = sizeof(T);
+  constexpr int GV = 16 / ES;                          // elements per slot
+  constexpr int64_t TE = gather_tile_elems<T>();       // elements per tile
+  constexpr int GS = static_cast<int>(TE / (kThreads * GV));
+  static_assert(GS >= 1 && TE == int64_t(GS) * kThreads * GV, "gather tile shape");
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
     int s = 0;
     while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
     const XSeg sg = a.seg[s];
     const int64_t lt = t - sg.tile0;
     int j0 = -1;
-    for (int j = 0; j < VE && j0 < 0; ++j)
-      if (aligned(sg.src + j * ES, VE * ES) && aligned(sg.dst + j * ES, VE * ES)) j0 = j;
+    for (int j = 0; j < GV && j0 < 0; ++j)
+      if (aligned(sg.src + j * ES, 16) && aligned(sg.dst + j * ES, 16)) j0 = j;
     const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    const int64_t rel0 = (j0 > 0 ? j0 - GV : 0) + lt * TE;
     const uint64_t bs = sg.src + rel0 * ES, bd = sg.dst + rel0 * ES;
-    Vec x[kSlots];
-    bool full[kSlots];
+    u32x4 x[GS];
+    bool full[GS];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < GS; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
-      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
-      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
-      if (full[u]) x[u] = ld_tile<Vec>(bs, slot * VE * ES);
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * GV;
+      full[u] = vec && rel >= 0 && rel + GV <= sg.numel;
+      if (full[u]) x[u] = ld_tile<u32x4>(bs, slot * 16);
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < GS; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
-      const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
+      const int64_t rel = rel0 + static_cast<int64_t>(slot) * GV;
       if (full[u]) {
-        st_tile<Vec>(bd, slot * VE * ES, x[u]);
-      } else if (rel < sg.numel && rel + VE > 0) {
+        st_tile<u32x4>(bd, slot * 16, x[u]);
+      } else if (rel < sg.numel && rel + GV > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
-        const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
+        const int64_t e1 = rel + GV < sg.numel ? rel + GV : sg.numel;
         for (int64_t e = e0; e < e1; ++e)
           reinterpret_cast<T*>(sg.dst)[e] = reinterpret_cast<const T*>(sg.src)[e];
       }
@@ -1280,7 +1291,9 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
       g.dst = reinterpret_cast<uint64_t>(out) + static_cast<uint64_t>(lo - out_base) * es;
       g.numel = hi - lo;
       g.tile0 = tiles;
-      tiles += tiles_for(g.numel);
+      // + one slot: a segment whose start is not slot-aligned spans one more.
+      const int64_t te = es == 2 ? gather_tile_elems<uint16_t>() : gather_tile_elems<float>();
+      tiles += (g.numel + 16 / static_cast<int64_t>(es) - 1 + te - 1) / te;
     }
     a.nseg = n;
     a.total_tiles = tiles;
