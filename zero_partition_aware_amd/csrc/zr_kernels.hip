@@ -89,21 +89,43 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ device helpers
 
+// Every buffer the library touches is device (global) memory.  Addressing it
+// through global-address-space pointers lets the compiler use global_load /
+// global_store with a uniform 64-bit base and a 32-bit lane offset instead of
+// flat instructions with a 64-bit address per lane.
+#define ZR_GLOBAL __attribute__((address_space(1)))
 template <typename T>
-__device__ __forceinline__ T ld_stream(const void* p) {
+__device__ __forceinline__ const ZR_GLOBAL T* gptr(const void* p) {
+  return (const ZR_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ ZR_GLOBAL T* gptr(void* p) {
+  return (ZR_GLOBAL T*)(p);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const ZR_GLOBAL T* p) {
 #if ZR_NT_LOADS
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  return __builtin_nontemporal_load(p);
 #else
-  return *reinterpret_cast<const T*>(p);
+  return *p;
 #endif
 }
 template <typename T>
-__device__ __forceinline__ void st_stream(void* p, T v) {
+__device__ __forceinline__ void st_global(ZR_GLOBAL T* p, T v) {
 #if ZR_NT_STORES
-  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+  __builtin_nontemporal_store(v, p);
 #else
-  *reinterpret_cast<T*>(p) = v;
+  *p = v;
 #endif
+}
+template <typename T>
+__device__ __forceinline__ T ld_stream(const void* p) {
+  return ld_global<T>(gptr<T>(p));
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(void* p, T v) {
+  st_global<T>(gptr<T>(p), v);
 }
 
 // Slot loads/stores relative to a per-tile stream base (uniform across the
@@ -119,7 +141,8 @@ __device__ __forceinline__ V ld_tile(uint64_t base, uint32_t off) {
   else
     return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, ZR_NT_LOADS ? 2 : 0));
 #else
-  return ld_stream<V>(reinterpret_cast<const void*>(base + off));
+  const ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<const void*>(base)) + off;
+  return ld_global<V>(reinterpret_cast<const ZR_GLOBAL V*>(b));
 #endif
 }
 template <typename V>
@@ -132,7 +155,8 @@ __device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
   else
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, ZR_NT_STORES ? 2 : 0);
 #else
-  st_stream<V>(reinterpret_cast<void*>(base + off), v);
+  ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<void*>(base)) + off;
+  st_global<V>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
 #endif
 }
 
@@ -301,12 +325,32 @@ __device__ __forceinline__ float reduce_one(const RedArgs& a, int rr, int64_t f)
   return acc;
 }
 
+// A value every lane of the wave holds, moved to a scalar register.  Segment
+// tables live in device memory and are read with vector loads; broadcasting
+// the fields tells the compiler they are uniform, so stream bases stay in
+// scalar registers and the slot accesses take a scalar base plus a 32-bit
+// lane offset.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int32_t uniform32(int32_t x) {
+  return static_cast<int32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x)));
+}
+__device__ __forceinline__ Seg load_seg(const Seg* p) {
+  const Seg s = *p;
+  return Seg{uniform64(s.flat), uniform64(s.part), uniform64(s.numel),
+             uniform64(s.tile0), uniform32(s.dst), uniform32(s.pad)};
+}
+
 // Tile -> segment by binary search over the segments' first-tile indices.
 __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (segs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
+    if (uniform64(segs[mid].tile0) <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -329,7 +373,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
   const int rr = R > 0 ? R : a.R;
 
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    const Seg sg = a.segs[find_seg(a.segs, a.nseg, t)];
+    const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
 
     // First offset j (0 <= j < 4) at which every stream is slot-aligned.
@@ -574,7 +618,7 @@ struct CopyArgs {
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    const Seg sg = a.segs[find_seg(a.segs, a.nseg, t)];
+    const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
     const float* s = a.src + sg.flat;
     float* d = a.dst + sg.part;
