@@ -377,6 +377,8 @@ def run_overlap(torch, zr, workloads, args):
                            "hidden_fraction": max(0.0, (t_ser - t_ovl) / t_red),
                            "overlap_bitwise_equal_serial": same,
                            "equal_across_bucket_sizes": same_across_b}
+        print(f"overlap B={B}: {nb} buckets, serial {1e3 * t_ser:.1f} ms, "
+              f"overlapped {1e3 * t_ovl:.1f} ms, equal {same}", file=sys.stderr, flush=True)
         del mg, others, reps, master0, state
         destroy_streams()
         torch.cuda.empty_cache()
