@@ -518,8 +518,13 @@ def setup_copy(torch, zr, workloads):
 def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
     """Time the CPU oracle (plan-driven reduce-scatter, Adam, bf16 writeback)
     on every rank's partition of the step (the whole step of all R ranks),
-    single-threaded numpy, inputs already on the host (copies untimed)."""
+    inputs already on the host (copies untimed).  Two runs of the same
+    oracle code: one thread, ranks one after another; then one thread per
+    rank (up to the host cores available), all ranks at once -- numpy's
+    elementwise loops release the interpreter lock, so the threads run on
+    separate cores."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle.adam import adam_oracle
     from oracle.bf16 import bf16_rne_oracle
     from oracle.plan import plan_oracle
@@ -527,23 +532,38 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
 
     ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
     z = np.zeros(P, np.float32)
+    wins = [[r[k * P:(k + 1) * P].cpu().view(torch.int16).numpy().view(np.uint16)
+             for r in reps] for k in range(R)]
+    masters = [workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                       w.master_sigma, "cuda").cpu().numpy()
+               for k in range(R)]
+
+    def one_rank(k):
+        g = reduce_scatter_oracle(ref, 0, wins[k], True, dst=k, flat_bases=[k * P] * R)[k]
+        th1, _, _ = adam_oracle(g, masters[k], z, z, step=1, **HP)
+        bf16_rne_oracle(th1)
+
     total = 0.0
     for k in range(R):
-        win = [r[k * P:(k + 1) * P].cpu().view(torch.int16).numpy().view(np.uint16)
-               for r in reps]
-        th = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
-                                     w.master_sigma, "cuda").cpu().numpy()
         t0 = time.perf_counter()
-        g = reduce_scatter_oracle(ref, 0, win, True, dst=k, flat_bases=[k * P] * R)[k]
-        th1, m1, v1 = adam_oracle(g, th, z, z, step=1, **HP)
-        bf16_rne_oracle(th1)
+        one_rank(k)
         total += time.perf_counter() - t0
+    avail = len(os.sched_getaffinity(0))
+    threads = max(1, min(R, avail))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda k: None, range(threads)))          # start the threads
+        t0 = time.perf_counter()
+        list(ex.map(one_rank, range(R)))
+        par = time.perf_counter() - t0
     byts = (R * 2 + 26) * P * R
     return {"value": round(byts / total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "elements_per_s": round(P * R / total), "seconds": round(total, 3),
             "sample": f"all {R} ranks' partitions of the step: {R} x {P} elements x {R} bf16 "
                       "replicas (reduce-scatter + Adam + bf16 writeback), numpy single thread",
-            "host_cores_available": len(os.sched_getaffinity(0))}
+            "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
+                         "elements_per_s": round(P * R / par), "seconds": round(par, 3),
+                         "sample": f"the same {R} partitions, one thread per rank"},
+            "host_cores_available": avail}
 
 
 # --------------------------------------------------------------------- main
