@@ -199,6 +199,47 @@ def test_fused_equals_unfused_and_oracle(seed, is_bf16):
             assert (host_f32(fth)[first:] == 0).all()
 
 
+# Element offsets of (replicas, master / m / v / reduced-grad outputs, bf16
+# param) inside their allocations.  Each nonzero choice gives the first
+# segment of some partition a nonzero tile phase (replica tiles moved onto
+# whole 128-byte lines, or one slot phase shared by every stream), so that
+# segment's first tile starts before partition offset 0 and the per-tile
+# stream bases are formed from a negative element offset.
+@pytest.mark.parametrize("is_bf16", [True, False])
+@pytest.mark.parametrize("offs", [(0, 0, 0), (32, 0, 0), (1, 1, 1), (3, 3, 3),
+                                  (33, 1, 1), (17, 0, 0)])
+def test_tile_phase_at_partition_start(is_bf16, offs):
+    ro, so, po = offs
+    numels, R = [12345, 7654], 4                 # 19,999 elements: P = 5000, 1 pad
+    ref = plan_oracle(numels, [0, 0], [(R, 1)], 1 << 30)
+    plan = zr.zr_plan_buckets(numels, [0, 0], [(R, 1)], 1 << 30)
+    P = ref.groups[0].part_numel
+    rng = np.random.default_rng(7 * sum(offs) + int(is_bf16))
+    reps = [_draw(rng, ref.groups[0].total, is_bf16, sigma=1e-3) for _ in range(R)]
+    dreps = [to_dev(x, ro) for x in reps]
+    want_g = reduce_scatter_oracle(ref, 0, reps, is_bf16)
+    for k in range(R):
+        th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(P) * 1e-4).astype(np.float32)
+        v = np.abs(rng.standard_normal(P) * 1e-8).astype(np.float32)
+        first = max(0, min(P, ref.groups[0].total - k * P))
+        th[first:] = m[first:] = v[first:] = 0.0
+        dth, dm, dv = to_dev(th, so), to_dev(m, so), to_dev(v, so)
+        pb = torch.zeros(P + po + 8, dtype=torch.bfloat16, device="cuda")[po: po + P]
+        go = empty_f32(P, so)
+        zr.zr_reduce_scatter_adam(plan, 0, -1, k, dreps, dth, dm, dv, pb, go, step=3, **HP)
+        out = empty_f32(P, so)
+        zr.zr_reduce_scatter_local(plan, 0, -1, k, dreps, [out])
+        assert_bits_equal(host_f32(go), want_g[k], f"fused grad, rank {k}")
+        assert_bits_equal(host_f32(out), want_g[k], f"reduced grad, rank {k}")
+        w_th, w_m, w_v = adam_oracle(want_g[k], th, m, v, step=3, **HP)
+        got_th = host_f32(dth)
+        assert_within(got_th, w_th, what=f"master, rank {k}")
+        assert_within(host_f32(dm), w_m, what=f"m, rank {k}")
+        assert_within(host_f32(dv), w_v, atol=0.0, what=f"v, rank {k}")
+        assert np.array_equal(host_u16(pb), bf16_rne_oracle(got_th)), f"bf16 param, rank {k}"
+
+
 @pytest.mark.parametrize("is_bf16", [True, False])
 def test_ipg_random_and_integer(is_bf16):
     numels = [4096 * 2 + 3, 5, 11111, 1, 777]

@@ -78,6 +78,10 @@ namespace {
 constexpr int kThreads = ZR_THREADS;
 constexpr int64_t kTileElems = ZR_TILE_ELEMS;
 constexpr int VE = 4;  // elements per lane slot
+// Cache-line size the reduce kernels align replica tiles to, and the largest
+// tile shift that alignment can need (a bf16 line minus one element).
+constexpr int64_t kLineBytes = 128;
+constexpr int64_t kMaxLineShift = kLineBytes / 2 - 1;
 constexpr int kSlots = static_cast<int>(kTileElems / (kThreads * VE));
 static_assert(kSlots >= 1 && kTileElems == int64_t(kSlots) * kThreads * VE,
               "a tile must be a whole number of lane slots");
@@ -376,9 +380,9 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
 
-    // First offset j (0 <= j < 4) at which every stream is slot-aligned.
-    int j0 = -1;
-    for (int j = 0; j < VE && j0 < 0; ++j) {
+    // Every stream is slot-aligned at segment offset j (VE elements of 4 or
+    // 2 bytes land on one 16- or 8-byte access).
+    auto slot_aligned = [&](int64_t j) {
       bool ok = true;
       if (!sg.pad)
         for (int r = 0; r < rr; ++r)
@@ -389,25 +393,53 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.m) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.v) + p4, 16);
-        if (a.pbf16) ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) + p4 / 2, 8);
+        if (a.pbf16)
+          ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) +
+                                 static_cast<uint64_t>(sg.part + j) * 2, 8);
         if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, 16);
       } else {
         ok = ok && aligned(a.out[sg.dst] + p4, 16);
       }
-      if (ok) j0 = j;
+      return ok;
+    };
+    // Tile phase.  Tiles start at segment offsets congruent to ph modulo
+    // `period` elements, shifted down by `shift` so the first tile begins at
+    // or before offset 0.  Preferred: the phase that puts replica 0's tiles
+    // on whole 128-byte lines (the replicas are most of the bytes read; a
+    // tile boundary inside a line makes two workgroups fetch that line).
+    // Otherwise the first phase below VE at which every stream is
+    // slot-aligned; if there is none the segment goes element by element.
+    int64_t ph = -1, period = VE;
+    if (!sg.pad) {
+      constexpr int64_t kLineElems = kLineBytes / sizeof(InT);
+      const uint64_t b0 = (a.in[0] + static_cast<uint64_t>(sg.flat) * sizeof(InT)) % kLineBytes;
+      const int64_t cand = static_cast<int64_t>((kLineBytes - b0) % kLineBytes / sizeof(InT));
+      if (cand < sg.numel && slot_aligned(cand)) {
+        ph = cand;
+        period = kLineElems;
+      }
     }
-    const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
+    for (int64_t j = 0; j < VE && ph < 0; ++j)
+      if (slot_aligned(j)) ph = j;
+    const bool vec = ph >= 0;
+    const int64_t shift = vec ? (period - ph) % period : 0;
+    const int64_t rel0 = lt * kTileElems - shift;
 
     // Per-tile stream bases: element rel0 of the segment in every stream.
+    // sg.part + rel0 (and sg.flat + rel0) can be negative for a segment's
+    // first tile; the byte offsets are formed by multiplying the signed
+    // element offset, so they wrap modulo 2^64 and every lane's address
+    // (base + its non-negative slot offset) comes out exact.  Never derive
+    // one from another by division.
     const uint64_t in_off = static_cast<uint64_t>(sg.flat + rel0) * sizeof(InT);
     const uint64_t p4 = static_cast<uint64_t>(sg.part + rel0) * 4;
+    const uint64_t p2 = static_cast<uint64_t>(sg.part + rel0) * 2;
     uint64_t b_master = 0, b_m = 0, b_v = 0, b_pb = 0, b_go = 0, b_out = 0;
     if constexpr (kFused) {
       b_master = reinterpret_cast<uint64_t>(a.master) + p4;
       b_m = reinterpret_cast<uint64_t>(a.m) + p4;
       b_v = reinterpret_cast<uint64_t>(a.v) + p4;
-      b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + p4 / 2 : 0;
+      b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + p2 : 0;
       b_go = a.gout ? reinterpret_cast<uint64_t>(a.gout) + p4 : 0;
     } else {
       b_out = a.out[sg.dst] + p4;
@@ -822,6 +854,11 @@ int64_t tiles_for(int64_t numel) {
   // + VE - 1: a segment whose start is not slot-aligned spans one more slot.
   return (numel + VE - 1 + kTileElems - 1) / kTileElems;
 }
+// Reduce-kernel segments may start their tiles up to kMaxLineShift elements
+// early (line-aligned replica tiles); the count covers the largest shift.
+int64_t reduce_tiles_for(int64_t numel) {
+  return (numel + kMaxLineShift + kTileElems - 1) / kTileElems;
+}
 
 // Launch tables derived from a plan: the host segment list (pure host data,
 // used for validation) and its device copy, both built on first use.
@@ -931,7 +968,7 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
   int64_t tiles = 0;
   for (auto& g : out) {
     g.tile0 = tiles;
-    tiles += tiles_for(g.numel);
+    tiles += kind == kReduceTable ? reduce_tiles_for(g.numel) : tiles_for(g.numel);
   }
   Seg sentinel{};
   sentinel.tile0 = tiles;
