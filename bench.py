@@ -509,7 +509,7 @@ def setup_copy(torch, zr, workloads):
     def step(i, timer):
         timer.launch(lambda: dst.copy_(src), "copy")
 
-    cfg = {"workload": "copy-4gib (torch copy_, practical ceiling)", "bytes_per_step": bytes_per_step}
+    cfg = {"workload": "copy-4gib (torch copy_, for reference)", "bytes_per_step": bytes_per_step}
     return step, bytes_per_step, n, cfg, {"copy": bytes_per_step}, "copy", None
 
 
