@@ -1,5 +1,5 @@
 """HIP path vs the oracle, element by element, at sizes the oracle finishes in
-seconds: several 4096-element tiles, ragged tails, misaligned pointers,
+seconds: many tiles, ragged tails, misaligned pointers,
 several groups, power-of-two and other divisors, special values."""
 
 import random

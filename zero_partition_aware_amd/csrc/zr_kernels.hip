@@ -3,8 +3,8 @@
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
 // LDS staging and no MFMA.  Work is cut into tiles of kTileElems elements of
 // one "segment" (a merged slice of the plan, a param's piece of an IPG
-// window, a ring chunk) -- 1024 elements, one 4-element slot per lane of a
-// 256-thread workgroup; by default every workgroup takes exactly one tile, so
+// window, a ring chunk) -- 512 elements, one 4-element slot per lane of a
+// 128-thread workgroup; by default every workgroup takes exactly one tile, so
 // the hardware dispatcher hands tiles out in address order and the set of
 // DRAM pages being touched at any moment stays compact.  A workgroup finds its
 // tile's segment by a binary search over per-segment tile offsets.
@@ -53,10 +53,10 @@ namespace {
 
 // Launch-shape constants (compile-time; the defaults are the tuned values).
 #ifndef ZR_TILE_ELEMS
-#define ZR_TILE_ELEMS 1024
+#define ZR_TILE_ELEMS 512
 #endif
 #ifndef ZR_THREADS
-#define ZR_THREADS 256
+#define ZR_THREADS 128
 #endif
 // Workgroups per CU when a grid-stride loop is wanted; 0 = one tile per WG.
 #ifndef ZR_GRID_PER_CU
