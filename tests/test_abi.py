@@ -5,6 +5,7 @@ the host-side validation of kernel calls rejects bad arguments without a GPU
 import ctypes
 import os
 import re
+import shutil
 import subprocess
 
 import pytest
@@ -148,3 +149,21 @@ def test_adam_rejects_negative_n():
     buf = _FakeTensor(0x100000, 16)
     with pytest.raises(zr.ZrError, match="n must"):
         zr.zr_adam_partition(buf, buf, buf, buf, n=-1, stream=0)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_plain_c_client_reproduces_the_golden_plan(tmp_path):
+    """include/zr.h compiles as C11 and a C program linked to libzr alone
+    reproduces the hand-derived tiny plan through the C ABI."""
+    exe = str(tmp_path / "plan_dump")
+    libdir = os.path.dirname(LIB)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-x", "c",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "native", "plan_dump.c"),
+                    "-x", "none", "-L", libdir, "-lzr", "-Wl,-rpath," + libdir, "-o", exe],
+                   check=True)
+    out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, check=True).stdout
+    golden = os.path.join(ROOT, "tests", "golden", "tiny_plan.txt")
+    want = [ln.strip() for ln in open(golden) if ln.strip() and not ln.startswith("#")]
+    assert out.strip().splitlines() == want
