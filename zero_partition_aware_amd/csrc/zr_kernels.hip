@@ -86,6 +86,42 @@ constexpr int kSlots = static_cast<int>(kTileElems / (kThreads * VE));
 static_assert(kSlots >= 1 && kTileElems == int64_t(kSlots) * kThreads * VE,
               "a tile must be a whole number of lane slots");
 constexpr int kIpgMaxSegs = 48;
+// Slots per lane in the IPG kernel (its tiles are kIpgSlots lane slots of
+// every thread).
+#ifndef ZR_IPG_SLOTS
+#define ZR_IPG_SLOTS 2
+#endif
+constexpr int kIpgSlots = ZR_IPG_SLOTS;
+constexpr int64_t kIpgTileElems = int64_t(kIpgSlots) * kThreads * VE;
+// Slots per lane of the standalone Adam, segmented copy and ring-step kernels,
+// and the all-gather's tile size in units of kTileElems fp32 elements.  Each
+// of these kernels covers kXSlots * kThreads * VE elements per tile.  Values
+// from A/B measurement: two slots pay for the light streams (copy +10%, ring
+// reduce-scatter step +2%, all-gather +2.5%, IPG +2.6%); Adam (-4%) and the
+// ring all-gather step (-1%) keep one.
+#ifndef ZR_ADAM_SLOTS
+#define ZR_ADAM_SLOTS 1
+#endif
+#ifndef ZR_COPY_SLOTS
+#define ZR_COPY_SLOTS 2
+#endif
+#ifndef ZR_RING_SLOTS
+#define ZR_RING_SLOTS 2
+#endif
+#ifndef ZR_RING_AG_SLOTS
+#define ZR_RING_AG_SLOTS 1
+#endif
+#ifndef ZR_GATHER_SLOTS
+#define ZR_GATHER_SLOTS 2
+#endif
+constexpr int kAdamSlots = ZR_ADAM_SLOTS;
+constexpr int64_t kAdamTileElems = int64_t(kAdamSlots) * kThreads * VE;
+constexpr int kCopySlots = ZR_COPY_SLOTS;
+constexpr int64_t kCopyTileElems = int64_t(kCopySlots) * kThreads * VE;
+constexpr int kRingSlots = ZR_RING_SLOTS;
+constexpr int64_t kRingTileElems = int64_t(kRingSlots) * kThreads * VE;
+constexpr int kRingAgSlots = ZR_RING_AG_SLOTS;
+constexpr int64_t kRingAgTileElems = int64_t(kRingAgSlots) * kThreads * VE;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -349,6 +385,20 @@ __device__ __forceinline__ Seg load_seg(const Seg* p) {
              uniform64(s.tile0), uniform32(s.dst), uniform32(s.pad)};
 }
 
+// Tile -> segment for a segment array passed in the kernel arguments
+// (ascending first-tile indices, segs[0].tile0 == 0): a binary search, so a
+// workgroup waits on at most log2(nseg) dependent scalar loads before its
+// first stream load.
+template <typename S>
+__device__ __forceinline__ int find_arg_seg(const S* segs, int nseg, int64_t t) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Tile -> segment by binary search over the segments' first-tile indices.
 __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
   int lo = 0, hi = nseg - 1;
@@ -528,20 +578,20 @@ struct AdamArgs {
 // Contiguous partition; kVec: every pointer 16-byte aligned (bf16 8-byte).
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
-  const int64_t ntiles = (a.n + kTileElems - 1) / kTileElems;
+  const int64_t ntiles = (a.n + kAdamTileElems - 1) / kAdamTileElems;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const uint64_t t4 = static_cast<uint64_t>(t) * kTileElems * 4;
+    const uint64_t t4 = static_cast<uint64_t>(t) * kAdamTileElems * 4;
     const uint64_t b_g = reinterpret_cast<uint64_t>(a.grad) + t4;
     const uint64_t b_master = reinterpret_cast<uint64_t>(a.master) + t4;
     const uint64_t b_m = reinterpret_cast<uint64_t>(a.m) + t4;
     const uint64_t b_v = reinterpret_cast<uint64_t>(a.v) + t4;
     const uint64_t b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + t4 / 2 : 0;
-    f32x4 g[kSlots], th[kSlots], mm[kSlots], vv[kSlots];
-    bool full[kSlots];
+    f32x4 g[kAdamSlots], th[kAdamSlots], mm[kAdamSlots], vv[kAdamSlots];
+    bool full[kAdamSlots];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kAdamSlots; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
-      const int64_t j = t * kTileElems + static_cast<int64_t>(slot) * VE;
+      const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       full[u] = kVec && j + VE <= a.n;
       if (full[u]) {
         g[u] = ld_tile<f32x4>(b_g, slot * 16);
@@ -551,9 +601,9 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kAdamSlots; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
-      const int64_t j = t * kTileElems + static_cast<int64_t>(slot) * VE;
+      const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       if (full[u]) {
         const float gg[4] = {g[u][0], g[u][1], g[u][2], g[u][3]};
         adam_slot(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
@@ -593,9 +643,7 @@ template <typename InT>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
   using Vec = typename In<InT>::Vec;
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    int s = 0;
-    while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
-    const IpgSeg sg = a.seg[s];
+    const IpgSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
     const uint64_t mg = reinterpret_cast<uint64_t>(a.main_grad);
     int j0 = -1;
@@ -604,12 +652,12 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
           aligned(mg + static_cast<uint64_t>(sg.dst + j) * 4, 16))
         j0 = j;
     const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
-    Vec x[kSlots];
-    f32x4 cur[kSlots];
-    bool full[kSlots];
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kIpgTileElems;
+    Vec x[kIpgSlots];
+    f32x4 cur[kIpgSlots];
+    bool full[kIpgSlots];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kIpgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
       if (full[u]) {
@@ -618,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kIpgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
         float g[4];
@@ -660,17 +708,17 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
     const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
-    f32x4 x[kSlots];
-    bool full[kSlots];
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kCopyTileElems;
+    f32x4 x[kCopySlots];
+    bool full[kCopySlots];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
       if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
         st_stream<f32x4>(d + rel, x[u]);
@@ -709,11 +757,11 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
     const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
-    f32x4 x[kSlots], y[kSlots];
-    bool full[kSlots];
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingTileElems;
+    f32x4 x[kRingSlots], y[kRingSlots];
+    bool full[kRingSlots];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kRingSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
       if (full[u]) {
@@ -722,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kRingSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
         st_stream<f32x4>(d + rel, f32x4{y[u][0] + x[u][0], y[u][1] + x[u][1],
@@ -758,7 +806,7 @@ struct XArgs {
 // (bf16 patterns) or float.  Used by the parameter all-gather.  There is no
 // fp32 stream to match, so a slot is one 16-byte vector of either type
 // (8 bf16 or 4 fp32) and a tile holds kGatherTileBytes.
-constexpr int64_t kGatherTileBytes = kTileElems * 4;
+constexpr int64_t kGatherTileBytes = kTileElems * 4 * ZR_GATHER_SLOTS;
 template <typename T>
 __host__ __device__ constexpr int64_t gather_tile_elems() {
   return kGatherTileBytes / static_cast<int64_t>(sizeof(T));
@@ -772,9 +820,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
   constexpr int GS = static_cast<int>(TE / (kThreads * GV));
   static_assert(GS >= 1 && TE == int64_t(GS) * kThreads * GV, "gather tile shape");
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-    int s = 0;
-    while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
-    const XSeg sg = a.seg[s];
+    const XSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
     int j0 = -1;
     for (int j = 0; j < GV && j0 < 0; ++j)
@@ -825,17 +871,17 @@ __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
     const bool vec = j0 >= 0;
-    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kTileElems;
-    f32x4 x[kSlots];
-    bool full[kSlots];
+    const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingAgTileElems;
+    f32x4 x[kRingAgSlots];
+    bool full[kRingAgSlots];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kRingAgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
       if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
     }
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < kRingAgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
         st_stream<f32x4>(d + rel, x[u]);
@@ -850,9 +896,10 @@ __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
 
 // ================================================================= host ===
 
-int64_t tiles_for(int64_t numel) {
-  // + VE - 1: a segment whose start is not slot-aligned spans one more slot.
-  return (numel + VE - 1 + kTileElems - 1) / kTileElems;
+// Tiles of `tile` elements covering a segment of numel elements; + VE - 1: a
+// segment whose start is not slot-aligned spans one more slot.
+int64_t tiles_for(int64_t numel, int64_t tile) {
+  return (numel + VE - 1 + tile - 1) / tile;
 }
 // Reduce-kernel segments may start their tiles up to kMaxLineShift elements
 // early (line-aligned replica tiles); the count covers the largest shift.
@@ -968,7 +1015,7 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
   int64_t tiles = 0;
   for (auto& g : out) {
     g.tile0 = tiles;
-    tiles += kind == kReduceTable ? reduce_tiles_for(g.numel) : tiles_for(g.numel);
+    tiles += kind == kReduceTable ? reduce_tiles_for(g.numel) : tiles_for(g.numel, kCopyTileElems);
   }
   Seg sentinel{};
   sentinel.tile0 = tiles;
@@ -1224,7 +1271,7 @@ extern "C" zr_status zr_adam_partition(const zr_adam* h, const float* grad, floa
   const bool vec = elem_aligned(grad, 16) && elem_aligned(master, 16) &&
                    elem_aligned(m, 16) && elem_aligned(v, 16) &&
                    (!param_bf16 || elem_aligned(param_bf16, 8));
-  const unsigned grid = grid_for((n + kTileElems - 1) / kTileElems, cus);
+  const unsigned grid = grid_for((n + kAdamTileElems - 1) / kAdamTileElems, cus);
   if (vec) adam_kernel<true><<<grid, kThreads, 0, stream>>>(a);
   else adam_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   return check_launch("adam_partition launch");
@@ -1282,7 +1329,7 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
       for (size_t i = b; i < e; ++i) {
         a.seg[i - b] = segs[i];
         a.seg[i - b].tile0 = tiles;
-        tiles += tiles_for(segs[i].numel);
+        tiles += tiles_for(segs[i].numel, kIpgTileElems);
       }
       a.nseg = static_cast<int32_t>(e - b);
       a.total_tiles = tiles;
@@ -1392,7 +1439,7 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
 // Shared validation of the ring steps.
 namespace {
 zr_status ring_args(float* const* rank_bufs, int32_t n_ranks, int64_t chunk_numel,
-                    int32_t step, RingArgs* a) {
+                    int32_t step, int64_t tile, RingArgs* a) {
   if (n_ranks < 2 || n_ranks > ZR_MAX_WORLD)
     return fail(ZR_ERR_INVALID, "n_ranks must lie in [2, ZR_MAX_WORLD]");
   if (step < 0 || step > n_ranks - 2) return fail(ZR_ERR_INVALID, "step out of range");
@@ -1412,7 +1459,7 @@ zr_status ring_args(float* const* rank_bufs, int32_t n_ranks, int64_t chunk_nume
   std::memset(a, 0, sizeof(*a));
   for (int k = 0; k < n_ranks; ++k) a->buf[k] = reinterpret_cast<uint64_t>(rank_bufs[k]);
   a->chunk = chunk_numel;
-  a->tiles_per_rank = tiles_for(chunk_numel);
+  a->tiles_per_rank = tiles_for(chunk_numel, tile);
   a->n = n_ranks;
   a->step = step;
   return ZR_OK;
@@ -1424,7 +1471,7 @@ extern "C" zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
                                      hipStream_t stream) {
   zr::clear_error();
   RingArgs a;
-  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, &a);
+  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, kRingAgTileElems, &a);
   if (st != ZR_OK || chunk_numel == 0) return st;
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
@@ -1438,7 +1485,7 @@ extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
                                      hipStream_t stream) {
   zr::clear_error();
   RingArgs a;
-  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, &a);
+  zr_status st = ring_args(rank_bufs, n_ranks, chunk_numel, step, kRingTileElems, &a);
   if (st != ZR_OK || chunk_numel == 0) return st;
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
