@@ -70,11 +70,6 @@ namespace {
 #ifndef ZR_NT_STORES
 #define ZR_NT_STORES 1
 #endif
-// 1: the vector path of the reduce kernels uses buffer instructions with a
-// per-tile resource (base = the tile's first element of each stream).
-#ifndef ZR_BUFFER_OPS
-#define ZR_BUFFER_OPS 0
-#endif
 constexpr int kThreads = ZR_THREADS;
 constexpr int64_t kTileElems = ZR_TILE_ELEMS;
 constexpr int VE = 4;  // elements per lane slot
@@ -170,34 +165,15 @@ __device__ __forceinline__ void st_stream(void* p, T v) {
 
 // Slot loads/stores relative to a per-tile stream base (uniform across the
 // workgroup) at a per-lane byte offset.
-constexpr int kTileBytes = static_cast<int>(kTileElems) * 4;
 template <typename V>
 __device__ __forceinline__ V ld_tile(uint64_t base, uint32_t off) {
-#if ZR_BUFFER_OPS
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0,
-                                                    kTileBytes, 0x00020000);
-  if constexpr (sizeof(V) == 8)
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, ZR_NT_LOADS ? 2 : 0));
-  else
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, ZR_NT_LOADS ? 2 : 0));
-#else
   const ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<const void*>(base)) + off;
   return ld_global<V>(reinterpret_cast<const ZR_GLOBAL V*>(b));
-#endif
 }
 template <typename V>
 __device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
-#if ZR_BUFFER_OPS
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0,
-                                                    kTileBytes, 0x00020000);
-  if constexpr (sizeof(V) == 8)
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, ZR_NT_STORES ? 2 : 0);
-  else
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, ZR_NT_STORES ? 2 : 0);
-#else
   ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<void*>(base)) + off;
   st_global<V>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
-#endif
 }
 
 __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
