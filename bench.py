@@ -243,7 +243,9 @@ def run_overlap(torch, zr, workloads, args):
     The plan is built over the Llama-3-8B list in gradient-ready order (last
     layer first).  Stream A runs the backward stand-in: for every param a
     weight-gradient GEMM (dY^T X over 2048 tokens, bf16, torch matmul) and
-    the IPG fill of that gradient into this rank's full fp32 main_grad.  As
+    the IPG fill of that gradient into this rank's full fp32 main_grad
+    (``--backward ipg``: the IPG fill alone, each gradient a view of one
+    pre-drawn bf16 buffer).  As
     soon as a bucket is complete its fused reduce-scatter + Adam for this
     rank's partition is launched on stream B after an event from stream A;
     the other 7 replicas' windows are resident.  Backward-only, reduce-only
@@ -255,6 +257,7 @@ def run_overlap(torch, zr, workloads, args):
     numels = [w.numels[p] for p in order]
     shapes = [w.shapes[p] for p in order]
     R, k, tok = 8, 0, args.tokens
+    ipg_only = args.backward == "ipg"
     dev = "cuda"
     hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime torch already holds
     created = []
@@ -280,6 +283,9 @@ def run_overlap(torch, zr, workloads, args):
     X = {i: (torch.randn(tok, i, device=dev) * 0.1).to(torch.bfloat16)
          for i in sorted({s[-1] for s in shapes})}
     dYt = (torch.randn(o_max, tok, device=dev) * 0.1).to(torch.bfloat16)
+    # IPG-only backward: every param's gradient is a view of one bf16 buffer.
+    gbuf = (workloads.device_normal(workloads.seed_for(name, 0, 5), max(numels), w.grad_sigma,
+                                    dev, "bf16") if ipg_only else None)
     results = {}
     ref_master = None
     s_full = torch.cuda.current_stream()      # serial reference on every CU
@@ -316,7 +322,9 @@ def run_overlap(torch, zr, workloads, args):
         def backward(on_bucket):
             done = 0
             for p, (ne, shp) in enumerate(zip(numels, shapes)):
-                if len(shp) == 2:
+                if ipg_only:
+                    g = gbuf[:ne]
+                elif len(shp) == 2:
                     g = torch.matmul(dYt[:shp[0]], X[shp[1]]).view(-1)
                 else:
                     g = X[shp[0]][0].clone()
@@ -387,6 +395,7 @@ def run_overlap(torch, zr, workloads, args):
     out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
            "higher_is_better": True, "data": "synthetic",
            "config": {"workload": "llama3-8b-overlap", "rank": k, "tokens": tok,
+                      "backward": "ipg" if ipg_only else "weight-gradient gemm + ipg",
                       "ready_order": "last layer first"},
            "overlap": results, "parity_ok": ok,
            "device": torch.cuda.get_device_name(0)}
@@ -582,6 +591,9 @@ def main():
     ap.add_argument("--buckets", type=lambda t: [int(float(x)) for x in t.split(",")],
                     default=[int(5e7), int(5e8)],
                     help="reduce_bucket_size values for --workload llama3-8b-overlap")
+    ap.add_argument("--backward", choices=["gemm", "ipg"], default="gemm",
+                    help="backward stand-in of llama3-8b-overlap: weight-gradient GEMMs "
+                         "plus IPG fills, or IPG fills alone")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="tokens of the backward GEMM stand-in (llama3-8b-overlap)")
     args = ap.parse_args()
