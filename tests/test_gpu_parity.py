@@ -264,6 +264,31 @@ def test_ipg_random_and_integer(is_bf16):
         assert_bits_equal(host_f32(dmg), mg, f"window {base}+{length}")
 
 
+@pytest.mark.parametrize("is_bf16", [True, False])
+def test_ipg_many_params_several_launches(is_bf16):
+    """130 params in one call: more segments than one launch carries (48), so
+    the call spans three launches and each workgroup's segment search runs
+    at full depth; params listed in shuffled order, windows clipping params
+    at both ends, gradient pointers misaligned by 0-3 elements."""
+    rng = np.random.default_rng(11 + int(is_bf16))
+    numels = [int(x) for x in rng.integers(1, 6000, size=130)]
+    numels[7] = 40000                                   # several tiles in one segment
+    n = len(numels)
+    plan = zr.zr_plan_buckets(numels, [0] * n, [(4, 1)], 1 << 30)
+    ref = plan_oracle(numels, [0] * n, [(4, 1)], 1 << 30)
+    ids = [int(i) for i in rng.permutation(n)]
+    total = ref.groups[0].padded
+    for base, length in [(0, total), (12345, total // 2), (total - 70001, 70001)]:
+        mg = np.zeros(length, np.float32)
+        dmg = to_dev(mg)
+        for mb in range(3):
+            grads = [_draw(rng, numels[p], is_bf16) for p in ids]
+            ipg_accumulate_oracle(mg, base, ref.param_offset, ids, grads, is_bf16)
+            zr.zr_ipg_accumulate(plan, ids, [to_dev(x, (i + mb) % 4) for i, x in enumerate(grads)],
+                                 dmg, window_base=base)
+        assert_bits_equal(host_f32(dmg), mg, f"window {base}+{length}")
+
+
 @pytest.mark.parametrize("n,chunk", [(8, 4096 * 3 + 5), (3, 1000), (2, 1)])
 def test_ring_steps(n, chunk):
     rng = np.random.default_rng(n)
