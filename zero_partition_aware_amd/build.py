@@ -33,14 +33,27 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def _code_text(path):
+    """A C/C++ source with its comments removed and whitespace collapsed: the
+    part of the file that reaches the compiler."""
+    import re
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash():
-    """Short hash of the kernel source and build flags: counter measurements
-    are only valid for the exact code they were taken on."""
+    """Short hash of the device code and its compile flags (comments and
+    whitespace excluded): counter measurements are only valid for the exact
+    code they were taken on."""
     import hashlib
     h = hashlib.sha256()
-    for path in (os.path.join(CSRC, "zr_kernels.hip"), os.path.abspath(__file__)):
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+    for path in (os.path.join(CSRC, "zr_kernels.hip"), os.path.join(CSRC, "zr_internal.h"),
+                 os.path.join(INCLUDE, "zr.h")):
+        h.update(_code_text(path).encode())
+    h.update(" ".join(HIP_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

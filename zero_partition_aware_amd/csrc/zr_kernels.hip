@@ -1,13 +1,16 @@
 // HIP kernels and their C-ABI entry points for CDNA4 (gfx950).
 //
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
-// LDS staging and no MFMA.  Work is cut into tiles of kTileElems elements of
-// one "segment" (a merged slice of the plan, a param's piece of an IPG
-// window, a ring chunk) -- 512 elements, one 4-element slot per lane of a
-// 128-thread workgroup; by default every workgroup takes exactly one tile, so
-// the hardware dispatcher hands tiles out in address order and the set of
-// DRAM pages being touched at any moment stays compact.  A workgroup finds its
-// tile's segment by a binary search over per-segment tile offsets.
+// LDS staging and no MFMA.  Work is cut into tiles of one "segment" (a merged
+// slice of the plan, a param's piece of an IPG window, a ring chunk): the
+// reduce and Adam kernels take 512 elements per 128-thread workgroup (one
+// 4-element slot per lane), the lighter IPG, copy, ring reduce-scatter and
+// all-gather kernels 1024 (two slots per lane).  By default every workgroup
+// takes exactly one tile, so the hardware dispatcher hands tiles out in
+// address order and the set of DRAM pages being touched at any moment stays
+// compact.  A workgroup finds its tile's segment by a binary search over
+// per-segment tile offsets.  Reduce-kernel tiles start where replica 0's
+// tiles sit on whole 128-byte lines, when the other streams allow it.
 //
 // Inside a tile each lane owns "slots" of four consecutive elements, and the
 // 64 lanes of a wavefront own 64 consecutive slots, so every load or store
