@@ -153,30 +153,38 @@ def test_moe_two_groups_fused_and_bucketed():
         T, P, R = info.total, info.part_numel, info.world
         reps = [workloads.device_normal(workloads.seed_for(name, r + 100 * g), T,
                                         w.grad_sigma, DEV) for r in range(R)]
-        k = R - 1
-        master = workloads.device_normal(workloads.seed_for(name, 10 * g + k, master=True), P,
-                                         w.master_sigma, DEV)
-        mb = master.clone()
-        idx = _sample(P, 20000, g, [s for s in ref.slices if s.dst == k and s.group == g])
-        th_s = _gather(master, idx)
-        m, v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
-        pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
-        gout = torch.empty(P, device=DEV)
-        zr.zr_reduce_scatter_adam(plan, g, -1, k, reps, master, m, v, pbf16, gout, **HP)
-        reps_s = [_gather(r_, k * P + idx) for r_ in reps]
-        _check_fused(reps_s, False, info.divisor, th_s, master, m, v, pbf16, gout, idx)
-        # The bucketed path (one fused call per bucket) gives the same bits.
-        mb_m, mb_v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
-        mb_p = torch.empty(P, dtype=torch.bfloat16, device=DEV)
-        for b in range(ref.num_buckets):
-            zr.zr_reduce_scatter_adam(plan, g, b, k, reps, mb, mb_m, mb_v, mb_p, None, **HP)
-        torch.cuda.synchronize()
-        assert torch.equal(mb.view(torch.int32), master.view(torch.int32))
-        assert torch.equal(mb_v.view(torch.int32), v.view(torch.int32))
-        assert torch.equal(mb_p.view(torch.int16), pbf16.view(torch.int16))
-        print(f"moe group {g} rank {k}: {idx.size} sampled elements ok, bucketed == whole")
-        del reps, master, mb, m, v, pbf16, gout, mb_m, mb_v, mb_p
+        for k in (0, R - 1):
+            _moe_rank(plan, ref, g, info, reps, k, name, w)
+        del reps
         _free()
+
+
+def _moe_rank(plan, ref, g, info, reps, k, name, w):
+    """Rank k of MoE group g: the fused call on sampled outputs against the
+    oracle, then the bucketed calls against the whole call bit for bit."""
+    P = info.part_numel
+    master = workloads.device_normal(workloads.seed_for(name, 10 * g + k, master=True), P,
+                                     w.master_sigma, DEV)
+    mb = master.clone()
+    idx = _sample(P, 20000, g, [s for s in ref.slices if s.dst == k and s.group == g])
+    th_s = _gather(master, idx)
+    m, v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
+    pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+    gout = torch.empty(P, device=DEV)
+    zr.zr_reduce_scatter_adam(plan, g, -1, k, reps, master, m, v, pbf16, gout, **HP)
+    reps_s = [_gather(r_, k * P + idx) for r_ in reps]
+    _check_fused(reps_s, False, info.divisor, th_s, master, m, v, pbf16, gout, idx)
+    # The bucketed path (one fused call per bucket) gives the same bits.
+    mb_m, mb_v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
+    mb_p = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+    for b in range(ref.num_buckets):
+        zr.zr_reduce_scatter_adam(plan, g, b, k, reps, mb, mb_m, mb_v, mb_p, None, **HP)
+    torch.cuda.synchronize()
+    assert torch.equal(mb.view(torch.int32), master.view(torch.int32))
+    assert torch.equal(mb_v.view(torch.int32), v.view(torch.int32))
+    assert torch.equal(mb_p.view(torch.int16), pbf16.view(torch.int16))
+    print(f"moe group {g} rank {k}: {idx.size} sampled elements ok, bucketed == whole")
+    del master, mb, m, v, pbf16, gout, mb_m, mb_v, mb_p
 
 
 def test_ring_1gib_eight_ranks():
