@@ -494,6 +494,81 @@ def setup_moe(torch, zr, workloads):
         {f"fused_g{g}": gr["bytes"] for g, gr in enumerate(groups)}, "fused_g1", None
 
 
+def setup_moe_bucketed(torch, zr, workloads, graph=False):
+    """The MoE step through the bucketed path of the pages' IPG design: for
+    rank 0 of each group, one reduce-scatter call per (bucket, group) that
+    has slices for that rank (269 buckets of 5e6 elements, both groups
+    interleaved), into the rank's fp32 gradient partition, then Adam over
+    each partition.  With ``graph`` the whole step is captured once in a HIP
+    graph (torch.cuda.CUDAGraph) and each step is one replay: the step is
+    launch-bound (hundreds of small launches), which is what graphs remove."""
+    name = "moe-16l"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    nb = zr.zr_plan_num_buckets(plan)
+    k = 0
+    groups = []
+    total_bytes = 0
+    for g, (R, sp) in enumerate(w.groups):
+        T, L, P, D = zr.zr_plan_group_info(plan, g)
+        reps = [workloads.device_normal(workloads.seed_for(name, r + 100 * g), T, w.grad_sigma,
+                                        "cuda") for r in range(R)]
+        master = workloads.device_normal(workloads.seed_for(name, 10 * g + k, master=True),
+                                         P, w.master_sigma, "cuda")
+        groups.append(dict(R=R, P=P, reps=reps, grad=torch.empty(P, device="cuda"),
+                           master=master, m=torch.zeros_like(master),
+                           v=torch.zeros_like(master),
+                           pbf16=torch.empty(P, dtype=torch.bfloat16, device="cuda")))
+        total_bytes += (R * 4 + 4 + 30) * P
+    # (bucket, group) selections holding slices for rank k, plus the last
+    # bucket of every group (it also writes the group's padding).
+    pairs = []
+    for b in range(nb):
+        sl = zr.zr_plan_slices(plan, b)
+        for g in range(len(groups)):
+            if b == nb - 1 or any(s[1] == g and s[2] == k for s in sl):
+                pairs.append((b, g))
+
+    def eager(t, timer):
+        for b, g in pairs:
+            gr = groups[g]
+            timer.launch(lambda: zr.zr_reduce_scatter_local(plan, g, b, k, gr["reps"],
+                                                            [gr["grad"]]), "reduce")
+        for gr in groups:
+            timer.launch(lambda: zr.zr_adam_partition(gr["grad"], gr["master"], gr["m"],
+                                                      gr["v"], gr["pbf16"], step=t, **HP),
+                         "adam")
+
+    # Per-launch bytes of each kind, averaged over the step's launches of it.
+    launch_bytes = {"reduce": round(sum((gr["R"] * 4 + 4) * gr["P"] for gr in groups) / len(pairs)),
+                    "adam": round(sum(30 * gr["P"] for gr in groups) / len(groups))}
+    cfg = {"workload": name + ("-bucketed-graph" if graph else "-bucketed"),
+           "params": len(w.numels), "groups": w.groups, "rank": k,
+           "reduce_bucket_size": w.reduce_bucket_size, "buckets": nb,
+           "reduce_launches_per_step": len(pairs), "adam_launches_per_step": len(groups),
+           "partition_elems": [gr["P"] for gr in groups], "grad_dtype": "fp32",
+           "bytes_per_step": total_bytes}
+    if not graph:
+        return (lambda i, timer: eager(i + 1, timer)), total_bytes, \
+            sum(gr["P"] for gr in groups), cfg, launch_bytes, "reduce", None
+
+    # Capture one step (Adam step number fixed at capture) after an eager
+    # step has built the plan's launch tables.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        eager(1, Timer())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        eager(1, Timer())
+    torch.cuda.synchronize()
+    cfg["graph"] = "one captured step per replay (Adam step number fixed at capture)"
+    return (lambda i, timer: timer.launch(cg.replay, "graph")), total_bytes, \
+        sum(gr["P"] for gr in groups), cfg, {"graph": total_bytes}, "graph", None
+
+
 def setup_ring(torch, zr, workloads):
     c = workloads.RING_1GIB
     N, M = c["ranks"], c["elems_per_rank"]
@@ -586,7 +661,8 @@ def main():
                     choices=["gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
                              "llama3-8b-overlap",
-                             "llama3-8b", "llama3-8b-ipg", "moe-16l", "ring-1gib", "copy"])
+                             "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
+                             "moe-16l-bucketed-graph", "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buckets", type=lambda t: [int(float(x)) for x in t.split(",")],
                     default=[int(5e7), int(5e8)],
@@ -618,6 +694,8 @@ def main():
              "ring-1gib-allreduce": setup_ring_allreduce,
              "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
              "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
+             "moe-16l-bucketed": setup_moe_bucketed,
+             "moe-16l-bucketed-graph": lambda *a: setup_moe_bucketed(*a, graph=True),
              "ring-1gib": setup_ring, "copy": setup_copy}[args.workload]
     step, bytes_per_step, elems_per_step, cfg, launch_bytes, dominant, cpu_leg = \
         setup(torch, zr, workloads)
