@@ -1,0 +1,110 @@
+"""Randomized parity: random plans (1-2 groups, R up to 17, sp dividing R,
+bucket sizes from 1 element to unbounded, align up to 64), random element
+offsets of every stream, bf16 or fp32 replicas; the fused and unfused calls
+on several ranks, the per-bucket calls composed, and IPG over a random
+window, each against the oracle (bit-exact; Adam within rel 1e-6 / abs
+1e-7; bf16 param = RNE of the GPU's own master)."""
+
+import random
+
+import numpy as np
+import pytest
+
+from oracle.adam import adam_oracle
+from oracle.bf16 import bf16_rne_oracle
+from oracle.ipg import ipg_accumulate_oracle
+from oracle.plan import plan_oracle
+from oracle.reduce import reduce_scatter_oracle
+from tests._lib import load
+
+pytestmark = pytest.mark.gpu
+
+zr = load()
+torch = pytest.importorskip("torch")
+from tests._gpu import (assert_bits_equal, assert_within, empty_f32, host_f32,  # noqa: E402
+                        host_u16, to_dev)
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def _draw(rng, n, bf16):
+    x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    if bf16:
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x
+
+
+def _random_case(seed):
+    """One random case; raises on the first mismatch."""
+    pr = random.Random(seed)
+    rng = np.random.default_rng(seed)
+    ng = pr.choice([1, 2])
+    groups = []
+    for _ in range(ng):
+        R = pr.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17])
+        sp = pr.choice([d for d in (1, 2, 3, 4) if R % d == 0])
+        groups.append((R, sp))
+    n = pr.randint(1, 20)
+    numels = [pr.choice([1, 2, 3, 63, 64, 65, 511, 512, 513, pr.randint(1, 40000)]) for _ in range(n)]
+    pg = [pr.randrange(ng) for _ in range(n)]
+    B = pr.choice([1, 7, 100, 1000, 4096, 7777, 30000, 1 << 30])
+    align = pr.choice([1, 1, 2, 8, 64])
+    bf16 = pr.random() < 0.5
+    ref = plan_oracle(numels, pg, groups, B, align)
+    plan = zr.zr_plan_buckets(numels, pg, groups, B, 0, align)
+    for g, info in enumerate(ref.groups):
+        if info.total == 0:
+            continue
+        P, R = info.part_numel, info.world
+        reps = [_draw(rng, info.total, bf16) for _ in range(R)]
+        ro = pr.randint(0, 70)
+        dreps = [to_dev(x, ro) for x in reps]
+        want = reduce_scatter_oracle(ref, g, reps, bf16)
+        for k in sorted({0, R - 1, pr.randrange(R)}):
+            so, po, go = pr.randint(0, 40), pr.randint(0, 40), pr.randint(0, 40)
+            th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+            m = (rng.standard_normal(P) * 1e-4).astype(np.float32)
+            v = np.abs(rng.standard_normal(P) * 1e-8).astype(np.float32)
+            first = max(0, min(P, info.total - k * P))
+            th[first:] = m[first:] = v[first:] = 0.0
+            dth, dm, dv = to_dev(th, so), to_dev(m, so), to_dev(v, so)
+            pb = torch.zeros(P + po + 8, dtype=torch.bfloat16, device="cuda")[po:po + P]
+            gout = empty_f32(P, go)
+            zr.zr_reduce_scatter_adam(plan, g, -1, k, dreps, dth, dm, dv, pb, gout, step=2, **HP)
+            out = empty_f32(P, pr.randint(0, 5))
+            zr.zr_reduce_scatter_local(plan, g, -1, k, dreps, [out])
+            assert_bits_equal(host_f32(gout), want[k], f"seed {seed} g{g} k{k} fused grad")
+            assert_bits_equal(host_f32(out), want[k], f"seed {seed} g{g} k{k} reduced grad")
+            w_th, w_m, w_v = adam_oracle(want[k], th, m, v, step=2, **HP)
+            got = host_f32(dth)
+            assert_within(got, w_th, what=f"seed {seed} master")
+            assert_within(host_f32(dm), w_m, what=f"seed {seed} m")
+            assert_within(host_f32(dv), w_v, atol=0.0, what=f"seed {seed} v")
+            assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"seed {seed} bf16"
+            # per-bucket calls compose to the whole
+            ob = empty_f32(P, 0)
+            for b in range(ref.num_buckets):
+                zr.zr_reduce_scatter_local(plan, g, b, k, dreps, [ob])
+            gb = host_f32(ob)
+            w = want[k].copy()
+            mask = ~np.isnan(w)
+            assert np.array_equal(gb[mask].view(np.uint32), w[mask].view(np.uint32)), \
+                f"seed {seed} per-bucket"
+        # IPG over a random window
+        base = pr.randint(0, max(0, info.padded - 1))
+        length = pr.randint(1, info.padded - base)
+        ids = [p for p in range(n) if pg[p] == g]
+        pr.shuffle(ids)
+        mg = np.zeros(length, np.float32)
+        dmg = to_dev(mg)
+        grads = [_draw(rng, numels[p], bf16) for p in ids]
+        if ids:
+            ipg_accumulate_oracle(mg, base, ref.param_offset, ids, grads, bf16)
+            zr.zr_ipg_accumulate(plan, ids, [to_dev(x, pr.randint(0, 5)) for x in grads], dmg,
+                                 window_base=base)
+            assert_bits_equal(host_f32(dmg), mg, f"seed {seed} ipg")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_case(seed):
+    _random_case(seed)
