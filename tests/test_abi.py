@@ -167,3 +167,28 @@ def test_plain_c_client_reproduces_the_golden_plan(tmp_path):
     golden = os.path.join(ROOT, "tests", "golden", "tiny_plan.txt")
     want = [ln.strip() for ln in open(golden) if ln.strip() and not ln.startswith("#")]
     assert out.strip().splitlines() == want
+
+
+def test_binding_checks_buffer_types_and_sizes():
+    """What an address cannot carry is checked by the binding before the C
+    call: element type and the number of elements the call touches."""
+    plan = _tiny_plan()
+    P = zr.zr_plan_group_info(plan, 0)[2]
+    reps = [_FakeTensor(0x100000 * (i + 1), 2278) for i in range(4)]
+    ok = _FakeTensor(0x900000, P)
+    short = _FakeTensor(0xA00000, P - 1)
+    with pytest.raises(zr.ZrError, match="master holds"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, short, ok, ok, stream=0)
+    with pytest.raises(zr.ZrError, match="param_bf16 must be bf16"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, ok, ok, ok, ok, stream=0)
+    with pytest.raises(zr.ZrError, match="part_out"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, 0, reps, [short], stream=0)
+    with pytest.raises(zr.ZrError, match="replica 1 must be fp32"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, 0,
+                                   [reps[0], _FakeTensor(0x200000, 2278, "bf16")] + reps[2:],
+                                   [ok], stream=0)
+    with pytest.raises(zr.ZrError, match="v holds"):
+        zr.zr_adam_partition(ok, ok, ok, short, n=P, stream=0)
+    with pytest.raises(zr.ZrError, match="rank_bufs"):
+        zr.zr_ring_rs_step([_FakeTensor(0x100000 * (i + 1), 63) for i in range(8)], 8, 0,
+                           stream=0)

@@ -102,3 +102,23 @@ def test_bucket_size_invariance_on_gpu(is_bf16):
         zr.zr_reduce_scatter_local(plan, 0, -1, -1, dreps, outs)
         for k in range(4):
             assert_bits_equal(host_f32(outs[k]), want[k], f"B={B} dst {k}")
+
+
+def test_binding_rejects_strided_and_host_tensors():
+    """A strided view or a host tensor never reaches the C call (the kernels
+    would read it as dense device memory); outputs stay untouched."""
+    plan = zr.zr_plan_buckets([1000], [0], [(2, 1)], 1 << 20)
+    P = zr.zr_plan_group_info(plan, 0)[2]
+    reps = [to_dev(np.ones(1000, np.float32)) for _ in range(2)]
+    master = torch.zeros(P, device="cuda")
+    m, v = torch.zeros(P, device="cuda"), torch.zeros(P, device="cuda")
+    strided = torch.zeros(2 * P, device="cuda")[::2]
+    with pytest.raises(zr.ZrError, match="contiguous"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, strided, m, v)
+    with pytest.raises(zr.ZrError, match="device tensor"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, torch.zeros(P), m, v)
+    with pytest.raises(zr.ZrError, match="replica 0 must be contiguous"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, 0,
+                                   [torch.ones(2000, device="cuda")[::2], reps[1]], [master])
+    torch.cuda.synchronize()
+    assert not master.any() and not m.any() and not v.any()

@@ -147,11 +147,45 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_DT_NAME = {ZR_FP32: "fp32", ZR_BF16: "bf16"}
+
+
+def _buf(t, name, dtype=None, min_numel=None):
+    """Checks one buffer argument and returns its address (None for None).
+
+    The C calls see only addresses, so what a pointer cannot carry is checked
+    here: a torch tensor must be a contiguous device tensor (a strided view
+    would be read as if it were dense), of the element type the call needs,
+    and hold at least the elements the call touches.  Violations raise
+    ZrError(ZR_ERR_INVALID) before anything is enqueued."""
+    if t is None:
+        return None
+    if torch is not None and isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise ZrError(ZR_ERR_INVALID, f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ZrError(ZR_ERR_INVALID, f"{name} must be a device tensor")
+    if dtype is not None and _dtype_code(t) != dtype:
+        raise ZrError(ZR_ERR_INVALID, f"{name} must be {_DT_NAME[dtype]}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ZrError(ZR_ERR_INVALID,
+                      f"{name} holds {t.numel()} elements; the call touches {min_numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _part_numel(plan, group):
+    """P_g of the plan's group, queried once per plan and group."""
+    P = plan.part_numel.get(group)
+    if P is None:
+        P = plan.part_numel[group] = zr_plan_group_info(plan, group)[2]
+    return P
+
+
 def _dtype_code(t):
-    import torch
-    if t.dtype == torch.bfloat16:
+    dt = t.dtype
+    if dt is torch.bfloat16:
         return ZR_BF16
-    if t.dtype == torch.float32:
+    if dt is torch.float32:
         return ZR_FP32
     return -1
 
@@ -174,6 +208,7 @@ class Plan:
 
     def __init__(self, handle):
         self._h = handle
+        self.part_numel = {}      # group -> P_g (the plan is immutable)
 
     @property
     def handle(self):
@@ -283,13 +318,15 @@ def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
     """grads[i]: tensor of param param_ids[i] (bf16 or fp32, all one dtype);
     main_grad: fp32 window tensor."""
     n = len(param_ids)
+    if len(grads) != n:
+        raise ZrError(ZR_ERR_INVALID, "param_ids and grads differ in length")
     ids = (c_i64 * max(n, 1))(*[int(p) for p in param_ids])
-    ptrs = (c_vp * max(n, 1))(*[g.data_ptr() for g in grads])
     dt = _dtype_code(grads[0]) if n else ZR_FP32
+    ptrs = (c_vp * max(n, 1))(*[_buf(g, f"grads[{i}]", dt).value for i, g in enumerate(grads)])
     wl = main_grad.numel() if window_len is None else int(window_len)
     _check(_lib.zr_ipg_accumulate(plan.handle, ids, ptrs, n, dt,
-                                  _ptr(main_grad), int(window_base), wl,
-                                  _stream(stream)))
+                                  _buf(main_grad, "main_grad", ZR_FP32, wl),
+                                  int(window_base), wl, _stream(stream)))
 
 
 def _replicas(reps):
@@ -298,8 +335,8 @@ def _replicas(reps):
     dt = None
     for i, r in enumerate(reps):
         t, base = (r, 0) if not isinstance(r, tuple) else r
-        arr[i] = zr_replica(t.data_ptr(), int(base), t.numel())
         dt = _dtype_code(t) if dt is None else dt
+        arr[i] = zr_replica(_buf(t, f"replica {i}", dt).value, int(base), t.numel())
     return arr, (ZR_FP32 if dt is None else dt)
 
 
@@ -308,7 +345,10 @@ def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
     """part_out: list of fp32 tensors (all destinations when dst == -1, else
     the one partition)."""
     arr, dt = _replicas(reps)
-    outs = (c_vp * max(len(part_out), 1))(*[t.data_ptr() for t in part_out])
+    P = _part_numel(plan, group)
+    outs = (c_vp * max(len(part_out), 1))(
+        *[_buf(t, f"part_out[{i}]", ZR_FP32, P).value if t is not None else None
+          for i, t in enumerate(part_out)])
     _check(_lib.zr_reduce_scatter_local(plan.handle, int(group), int(bucket),
                                         int(dst), arr, dt, outs,
                                         _stream(stream)))
@@ -316,17 +356,26 @@ def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
 
 def zr_copy_grads_in_partition(plan, group, bucket, dst, bucket_layout_src,
                                part_out, stream=None):
-    _check(_lib.zr_copy_grads_in_partition(plan.handle, int(group), int(bucket),
-                                           int(dst), _ptr(bucket_layout_src),
-                                           _ptr(part_out), _stream(stream)))
+    need = 0
+    if int(bucket) >= 0:
+        for s in zr_plan_slices(plan, bucket):
+            if s[1] == int(group) and s[2] == int(dst):
+                need = max(need, s[3] + s[6])
+    _check(_lib.zr_copy_grads_in_partition(
+        plan.handle, int(group), int(bucket), int(dst),
+        _buf(bucket_layout_src, "bucket_layout_src", ZR_FP32, need),
+        _buf(part_out, "part_out", ZR_FP32, _part_numel(plan, group)), _stream(stream)))
 
 
 def zr_adam_partition(grad, master, m, v, param_bf16=None, lr=1e-3, beta1=0.9,
                       beta2=0.999, eps=1e-8, step=1, n=None, stream=None):
     h = _adam(lr, beta1, beta2, eps, step)
     nn = master.numel() if n is None else int(n)
-    _check(_lib.zr_adam_partition(ctypes.byref(h), _ptr(grad), _ptr(master),
-                                  _ptr(m), _ptr(v), _ptr(param_bf16), nn,
+    need = max(nn, 0)
+    _check(_lib.zr_adam_partition(ctypes.byref(h), _buf(grad, "grad", ZR_FP32, need),
+                                  _buf(master, "master", ZR_FP32, need),
+                                  _buf(m, "m", ZR_FP32, need), _buf(v, "v", ZR_FP32, need),
+                                  _buf(param_bf16, "param_bf16", ZR_BF16, need), nn,
                                   _stream(stream)))
 
 
@@ -335,23 +384,30 @@ def zr_reduce_scatter_adam(plan, group, bucket, dst, reps, master, m, v,
                            beta2=0.999, eps=1e-8, step=1, stream=None):
     arr, dt = _replicas(reps)
     h = _adam(lr, beta1, beta2, eps, step)
+    P = _part_numel(plan, group)
     _check(_lib.zr_reduce_scatter_adam(plan.handle, int(group), int(bucket),
                                        int(dst), arr, dt, ctypes.byref(h),
-                                       _ptr(master), _ptr(m), _ptr(v),
-                                       _ptr(param_bf16), _ptr(grad_out),
+                                       _buf(master, "master", ZR_FP32, P),
+                                       _buf(m, "m", ZR_FP32, P), _buf(v, "v", ZR_FP32, P),
+                                       _buf(param_bf16, "param_bf16", ZR_BF16, P),
+                                       _buf(grad_out, "grad_out", ZR_FP32, P),
                                        _stream(stream)))
 
 
 def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
     n = len(rank_bufs)
-    arr = (c_vp * max(n, 1))(*[t.data_ptr() for t in rank_bufs])
+    need = max(int(chunk_numel), 0) * n
+    arr = (c_vp * max(n, 1))(*[_buf(t, f"rank_bufs[{i}]", ZR_FP32, need).value
+                               if t is not None else None for i, t in enumerate(rank_bufs)])
     _check(_lib.zr_ring_rs_step(arr, n, int(chunk_numel), int(step),
                                 _stream(stream)))
 
 
 def zr_ring_ag_step(rank_bufs, chunk_numel, step, stream=None):
     n = len(rank_bufs)
-    arr = (c_vp * max(n, 1))(*[t.data_ptr() for t in rank_bufs])
+    need = max(int(chunk_numel), 0) * n
+    arr = (c_vp * max(n, 1))(*[_buf(t, f"rank_bufs[{i}]", ZR_FP32, need).value
+                               if t is not None else None for i, t in enumerate(rank_bufs)])
     _check(_lib.zr_ring_ag_step(arr, n, int(chunk_numel), int(step), _stream(stream)))
 
 
@@ -360,8 +416,11 @@ def zr_all_gather_params(plan, group, parts, out, out_base=0, out_len=None,
     """parts: list of R_g partition tensors (bf16 or fp32); out: tensor that
     receives flat elements [out_base, out_base + out_len)."""
     n = len(parts)
-    arr = (c_vp * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in parts])
     dt = _dtype_code(out)
+    P = _part_numel(plan, group)
+    arr = (c_vp * max(n, 1))(*[(_buf(t, f"parts[{i}]", dt, P).value if t is not None else 0)
+                               for i, t in enumerate(parts)])
     ol = out.numel() if out_len is None else int(out_len)
-    _check(_lib.zr_all_gather_params(plan.handle, int(group), arr, dt, _ptr(out),
-                                     int(out_base), ol, _stream(stream)))
+    _check(_lib.zr_all_gather_params(plan.handle, int(group), arr, dt,
+                                     _buf(out, "out", dt, ol), int(out_base), ol,
+                                     _stream(stream)))
