@@ -455,7 +455,10 @@ def setup_llama(torch, zr, workloads, ipg=False):
             plan, 0, -1, k, reps, master, m, v, pbf16, None, step=i + 1, **HP), "fused")
 
     cfg.update(grad_dtype="fp32 main_grad", bytes_per_step=bytes_per_step)
-    return step, bytes_per_step, P, cfg, {"fused": bytes_per_step}, "fused", None
+    def cpu_leg():
+        return cpu_oracle_chunk(torch, mgs, master, P, R, D, 1 << 26)
+
+    return step, bytes_per_step, P, cfg, {"fused": bytes_per_step}, "fused", cpu_leg
 
 
 def setup_moe(torch, zr, workloads):
@@ -647,6 +650,50 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
             "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
                          "elements_per_s": round(P * R / par), "seconds": round(par, 3),
                          "sample": f"the same {R} partitions, one thread per rank"},
+            "host_cores_available": avail}
+
+
+def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
+    """Time the CPU oracle on a fixed chunk of one rank's share: the first
+    ``chunk`` partition elements lie inside one slice, so the oracle's
+    per-slice steps apply directly (rank-order pre-divided sum of the R fp32
+    replica values, Adam, bf16 writeback); inputs already on the host.  One
+    thread, then one thread per eighth of the chunk."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.adam import adam_oracle
+    from oracle.bf16 import bf16_rne_oracle
+    from oracle.reduce import rank_order_mean
+
+    n = min(chunk, P)
+    xs = [w_[:n].cpu().numpy() for w_ in windows]
+    th = master[:n].cpu().numpy()
+    z = np.zeros(n, np.float32)
+
+    def part(a, b):
+        g = rank_order_mean([x[a:b] for x in xs], D)
+        th1, _, _ = adam_oracle(g, th[a:b], z[a:b], z[a:b], step=1, **HP)
+        bf16_rne_oracle(th1)
+
+    t0 = time.perf_counter()
+    part(0, n)
+    one = time.perf_counter() - t0
+    avail = len(os.sched_getaffinity(0))
+    threads = max(1, min(8, avail))
+    cuts = [n * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda i: None, range(threads)))
+        t0 = time.perf_counter()
+        list(ex.map(lambda i: part(cuts[i], cuts[i + 1]), range(threads)))
+        par = time.perf_counter() - t0
+    byts = (R * 4 + 26) * n
+    return {"value": round(byts / one / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "elements_per_s": round(n / one), "seconds": round(one, 3),
+            "sample": f"the first {n} elements of rank 0's partition ({R} fp32 replicas; "
+                      "reduce + Adam + bf16 writeback), numpy single thread",
+            "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
+                         "elements_per_s": round(n / par), "seconds": round(par, 3),
+                         "sample": f"the same chunk in {threads} pieces, one thread each"},
             "host_cores_available": avail}
 
 
