@@ -493,8 +493,16 @@ def setup_moe(torch, zr, workloads):
            "reduce_bucket_size": w.reduce_bucket_size,
            "partition_elems": [gr["P"] for gr in groups], "divisors": [gr["D"] for gr in groups],
            "grad_dtype": "fp32", "bytes_per_step": total_bytes}
+
+    def cpu_leg():
+        # The expert group's rank 0 (the dominant launch): its partition
+        # starts at flat offset 0, so the replicas' first elements are its own.
+        gr = groups[1]
+        return cpu_oracle_chunk(torch, gr["reps"], gr["states"][0]["master"], gr["P"],
+                                gr["R"], gr["D"], 1 << 26)
+
     return step, total_bytes, sum(gr["P"] for gr in groups), cfg, \
-        {f"fused_g{g}": gr["bytes"] for g, gr in enumerate(groups)}, "fused_g1", None
+        {f"fused_g{g}": gr["bytes"] for g, gr in enumerate(groups)}, "fused_g1", cpu_leg
 
 
 def setup_moe_bucketed(torch, zr, workloads, graph=False):
@@ -689,8 +697,8 @@ def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
     byts = (R * 4 + 26) * n
     return {"value": round(byts / one / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "elements_per_s": round(n / one), "seconds": round(one, 3),
-            "sample": f"the first {n} elements of rank 0's partition ({R} fp32 replicas; "
-                      "reduce + Adam + bf16 writeback), numpy single thread",
+            "sample": f"the first {n} elements of rank 0's partition ({R} fp32 replicas, "
+                      f"divisor {D:g}; reduce + Adam + bf16 writeback), numpy single thread",
             "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
                          "elements_per_s": round(n / par), "seconds": round(par, 3),
                          "sample": f"the same chunk in {threads} pieces, one thread each"},
