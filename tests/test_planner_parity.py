@@ -118,3 +118,33 @@ def test_param_buckets_match_list_positions():
                     s.flat_offset + s.numel > ref.param_offset[p]}
             assert mine == set(range(first, last + 1))
             pos += ne
+
+
+hypothesis = pytest.importorskip("hypothesis")
+st = hypothesis.strategies
+
+
+@st.composite
+def _plans(draw):
+    ng = draw(st.integers(1, 3))
+    groups = []
+    for _ in range(ng):
+        sp = draw(st.sampled_from([1, 2, 3, 4]))
+        groups.append((sp * draw(st.integers(1, 16 // sp)), sp))
+    n = draw(st.integers(1, 60))
+    numels = draw(st.lists(st.integers(1, 100000), min_size=n, max_size=n))
+    pg = draw(st.lists(st.integers(0, ng - 1), min_size=n, max_size=n))
+    total = sum(numels)
+    lo = max(1, total // 20000)                 # at most ~20,000 buckets
+    B = draw(st.one_of(st.integers(lo, lo + 63), st.integers(lo, 2 * total)))
+    align = draw(st.sampled_from([1, 2, 4, 8, 16, 64]))
+    return numels, pg, groups, B, align
+
+
+@hypothesis.settings(max_examples=200, deadline=None, derandomize=True,
+                     suppress_health_check=list(hypothesis.HealthCheck))
+@hypothesis.given(_plans())
+def test_planner_matches_oracle_on_generated_plans(case):
+    """Property form of the comparison above (the planner equals the oracle on
+    every drawn list); a counterexample is shrunk to a minimal plan."""
+    _compare(*case)
