@@ -1,5 +1,6 @@
 """Pins for oracle O6 (fp32 -> bf16 round to nearest even) against torch's
-CPU conversion, a library routine, on a stratified sample of bit patterns."""
+CPU conversion, a library routine: on a stratified sample of bit patterns and
+on all 2^32 of them."""
 
 import numpy as np
 import torch
@@ -51,3 +52,25 @@ def test_hand_cases():
     for v, want in cases.items():
         got = bf16_rne_oracle(np.array([v], np.float32))[0]
         assert got == want, (v, hex(got), hex(want))
+
+
+def test_every_fp32_pattern():
+    """All 2^32 fp32 bit patterns, in chunks on the host's cores (numpy and
+    torch release the interpreter lock inside their loops): the oracle equals
+    torch's conversion on every non-NaN value, and every NaN stays NaN with
+    its sign and top payload bits."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 22
+
+    def run(i):
+        _compare(np.arange(i * chunk, (i + 1) * chunk, dtype=np.uint64).astype(np.uint32))
+
+    threads = max(1, min(8, len(os.sched_getaffinity(0))))
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, range((1 << 32) // chunk)))
+    finally:
+        torch.set_num_threads(prev)
