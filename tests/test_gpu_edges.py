@@ -42,6 +42,40 @@ def test_bf16_writeback_on_stratified_bit_patterns():
     assert np.array_equal(host_u16(pb), bf16_rne_oracle(got_th))
 
 
+def test_bf16_writeback_on_every_fp32_pattern():
+    """The same identity over all 2^32 fp32 bit patterns, drawn on the device
+    in chunks: theta comes back unchanged bit for bit (NaNs stay NaN) and the
+    bf16 output equals the oracle's rounding of the kernel's own theta."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 28
+    z = torch.zeros(chunk, device="cuda")
+    pb = torch.empty(chunk, dtype=torch.bfloat16, device="cuda")
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    piece = chunk // threads
+    for c in range((1 << 32) // chunk):
+        x = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda")
+        x = torch.where(x >= (1 << 31), x - (1 << 32), x).to(torch.int32)
+        th = x.view(torch.float32)
+        del x
+        zr.zr_adam_partition(z, th, z.clone(), z.clone(), pb, **HP)
+        got_th = host_f32(th)
+        got_pb = host_u16(pb)
+        bits = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32)
+
+        def check(i):
+            a, b = i * piece, (i + 1) * piece
+            gt = got_th[a:b]
+            nan = np.isnan(gt)
+            assert np.array_equal(np.isnan(bits[a:b].view(np.float32)), nan)
+            assert np.array_equal(gt.view(np.uint32)[~nan], bits[a:b][~nan])
+            assert np.array_equal(got_pb[a:b], bf16_rne_oracle(gt))
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(check, range(threads)))
+        del th
+
+
 def test_checkpoint_resume_is_bitwise():
     numels = [5000, 333, 12000]
     plan = zr.zr_plan_buckets(numels, [0] * 3, [(4, 1)], 7000)
