@@ -289,6 +289,48 @@ def test_ipg_many_params_several_launches(is_bf16):
         assert_bits_equal(host_f32(dmg), mg, f"window {base}+{length}")
 
 
+@pytest.mark.parametrize("sp", [1, 2])
+def test_two_replica_reduce_on_every_bf16_pair(sp):
+    """Two bf16 replicas holding every pair (a, b) of bf16 bit patterns (2^32
+    elements, drawn on the device in chunks), reduced with divisor 2 (sp 1) or
+    1 (sp 2): both partitions equal the oracle's rank-order pre-divided sum
+    bit for bit, subnormals, infinities and NaNs included."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.ipg import widen_bf16
+    from oracle.reduce import rank_order_mean
+    chunk = 1 << 28
+    plan = zr.zr_plan_buckets([chunk], [0], [(2, sp)], 1 << 30)
+    P = zr.zr_plan_group_info(plan, 0)[2]
+    D = 2 // sp
+    outs = [torch.empty(P, device="cuda") for _ in range(2)]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    piece = chunk // threads
+
+    def as_bf16(v):
+        return torch.where(v >= (1 << 15), v - (1 << 16), v).to(torch.int16).view(torch.bfloat16)
+
+    for c in range((1 << 32) // chunk):
+        idx = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda")
+        reps = [as_bf16(idx >> 16), as_bf16(idx & 0xFFFF)]
+        del idx
+        zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, outs)
+        got = np.concatenate([host_f32(o) for o in outs])
+        idx_h = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64)
+
+        def check(i):
+            a, b = i * piece, (i + 1) * piece
+            hi = (idx_h[a:b] >> np.uint64(16)).astype(np.uint16)
+            lo = (idx_h[a:b] & np.uint64(0xFFFF)).astype(np.uint16)
+            with np.errstate(all="ignore"):     # inf - inf and NaN inputs are part of the sweep
+                want = rank_order_mean([widen_bf16(hi), widen_bf16(lo)], D)
+            assert_bits_equal(got[a:b], want, f"pairs chunk {c} piece {i}")
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(check, range(threads)))
+        del reps
+
+
 @pytest.mark.parametrize("n,chunk", [(8, 4096 * 3 + 5), (3, 1000), (2, 1)])
 def test_ring_steps(n, chunk):
     rng = np.random.default_rng(n)
