@@ -331,6 +331,43 @@ def test_two_replica_reduce_on_every_bf16_pair(sp):
         del reps
 
 
+def test_ipg_on_every_bf16_pair():
+    """IPG with main_grad holding every bf16 value widened to fp32 against a
+    gradient holding every bf16 value (2^32 pairs, on the device in chunks):
+    main_grad + widen(grad) equals the oracle's IPG bit for bit."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.ipg import widen_bf16
+    chunk = 1 << 28
+    plan = zr.zr_plan_buckets([chunk], [0], [(2, 1)], 1 << 30)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    piece = chunk // threads
+
+    def as_bf16(v):
+        return torch.where(v >= (1 << 15), v - (1 << 16), v).to(torch.int16).view(torch.bfloat16)
+
+    for c in range((1 << 32) // chunk):
+        idx = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda")
+        mg = as_bf16(idx >> 16).float()
+        g = as_bf16(idx & 0xFFFF)
+        del idx
+        zr.zr_ipg_accumulate(plan, [0], [g], mg)
+        got = host_f32(mg)
+        idx_h = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64)
+
+        def check(i):
+            a, b = i * piece, (i + 1) * piece
+            want = widen_bf16((idx_h[a:b] >> np.uint64(16)).astype(np.uint16)).copy()
+            lo = (idx_h[a:b] & np.uint64(0xFFFF)).astype(np.uint16)
+            with np.errstate(all="ignore"):
+                ipg_accumulate_oracle(want, 0, [0], [0], [lo], True)
+            assert_bits_equal(got[a:b], want, f"ipg pairs chunk {c} piece {i}")
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(check, range(threads)))
+        del mg, g
+
+
 @pytest.mark.parametrize("n,chunk", [(8, 4096 * 3 + 5), (3, 1000), (2, 1)])
 def test_ring_steps(n, chunk):
     rng = np.random.default_rng(n)
