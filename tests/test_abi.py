@@ -151,18 +151,24 @@ def test_adam_rejects_negative_n():
         zr.zr_adam_partition(buf, buf, buf, buf, n=-1, stream=0)
 
 
-@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
-def test_plain_c_client_reproduces_the_golden_plan(tmp_path):
-    """include/zr.h compiles as C11 and a C program linked to libzr alone
-    reproduces the hand-derived tiny plan through the C ABI."""
-    exe = str(tmp_path / "plan_dump")
+def _c_client(tmp_path, name):
+    """Compiles tests/native/<name>.c as C11 against include/zr.h and libzr."""
+    exe = str(tmp_path / name)
     libdir = os.path.dirname(LIB)
     subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-x", "c",
                     "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include",
-                    os.path.join(ROOT, "tests", "native", "plan_dump.c"),
+                    os.path.join(ROOT, "tests", "native", name + ".c"),
                     "-x", "none", "-L", libdir, "-lzr", "-Wl,-rpath," + libdir, "-o", exe],
                    check=True)
+    return exe
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_plain_c_client_reproduces_the_golden_plan(tmp_path):
+    """include/zr.h compiles as C11 and a C program linked to libzr alone
+    reproduces the hand-derived tiny plan through the C ABI."""
+    exe = _c_client(tmp_path, "plan_dump")
     out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, check=True).stdout
     golden = os.path.join(ROOT, "tests", "golden", "tiny_plan.txt")
     want = [ln.strip() for ln in open(golden) if ln.strip() and not ln.startswith("#")]
@@ -192,3 +198,13 @@ def test_binding_checks_buffer_types_and_sizes():
     with pytest.raises(zr.ZrError, match="rank_bufs"):
         zr.zr_ring_rs_step([_FakeTensor(0x100000 * (i + 1), 63) for i in range(8)], 8, 0,
                            stream=0)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_plain_c_client_sees_documented_errors(tmp_path):
+    """From C: invalid plans and kernel calls return ZR_ERR_INVALID with a
+    message in zr_last_error(), before anything is enqueued."""
+    exe = _c_client(tmp_path, "abi_errors")
+    proc = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert proc.returncode == 0, proc.stdout
+    assert proc.stdout.strip().endswith("all ok")
