@@ -164,6 +164,27 @@ def setup_gpt2_unfused(torch, zr, workloads, copy_only=False):
     return step, rb + ab, P, cfg, {"reduce": rb, "adam": ab}, "reduce", None
 
 
+def setup_llama_copy(torch, zr, workloads):
+    """The standalone copy into the partition (a4) at a size where a launch's
+    ramp does not matter: Llama-3-8B's first bucket (5e8 elements, all of it
+    inside rank 0's partition), bucket layout -> partition, 4 GB per launch."""
+    name = "llama3-8b"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    T, L, P, D = zr.zr_plan_group_info(plan, 0)
+    n = sum(s[6] for s in zr.zr_plan_slices(plan, 0) if s[2] == 0)
+    src = workloads.device_normal(workloads.seed_for(name, 0, 7), w.reduce_bucket_size,
+                                  w.grad_sigma, "cuda")
+    part = torch.empty(P, device="cuda")
+
+    def step(i, timer):
+        timer.launch(lambda: zr.zr_copy_grads_in_partition(plan, 0, 0, 0, src, part), "copy")
+
+    cfg = {"workload": name + "-copy-in-partition", "copied_elems": n,
+           "bytes_per_step": 8 * n, "share": "rank 0's slices of the first bucket"}
+    return step, 8 * n, n, cfg, {"copy": 8 * n}, "copy", None
+
+
 def setup_gpt2_allgather(torch, zr, workloads):
     """Parameter all-gather after the update: one rank rebuilds the full bf16
     parameter vector (124,439,808 elements) from the 8 updated partitions."""
@@ -717,7 +738,7 @@ def main():
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
                              "llama3-8b-overlap",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
-                             "moe-16l-bucketed-graph", "ring-1gib", "copy"])
+                             "moe-16l-bucketed-graph", "llama3-8b-copy", "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buckets", type=lambda t: [int(float(x)) for x in t.split(",")],
                     default=[int(5e7), int(5e8)],
@@ -750,6 +771,7 @@ def main():
              "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
              "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
              "moe-16l-bucketed": setup_moe_bucketed,
+             "llama3-8b-copy": setup_llama_copy,
              "moe-16l-bucketed-graph": lambda *a: setup_moe_bucketed(*a, graph=True),
              "ring-1gib": setup_ring, "copy": setup_copy}[args.workload]
     step, bytes_per_step, elems_per_step, cfg, launch_bytes, dominant, cpu_leg = \
