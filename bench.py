@@ -69,6 +69,43 @@ class Timer:
         fn()
 
 
+class EventTimer(Timer):
+    """Records a pair of HIP events around every launch of one label (other
+    labels are skipped), for per-launch durations."""
+
+    def __init__(self, torch, only, limit):
+        super().__init__(only)
+        self.torch, self.limit, self.pairs = torch, limit, []
+
+    def launch(self, fn, label):
+        if label != self.only or len(self.pairs) >= self.limit:
+            return
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.append((e0, e1))
+
+
+def median_launch_us(torch, step, first, label, reps=21):
+    """Median duration of ``reps`` launches of one label, each bracketed by
+    its own HIP events (three unrecorded warm-up launches first)."""
+    for i in range(3):
+        step(first + i, Timer(only=label))
+    timer = EventTimer(torch, label, reps)
+    i = first + 3
+    while len(timer.pairs) < reps:
+        n = len(timer.pairs)
+        step(i, timer)
+        i += 1
+        if len(timer.pairs) == n:       # the label is not launched by this step
+            break
+    torch.cuda.synchronize()
+    d = sorted(1e3 * a.elapsed_time(b) for a, b in timer.pairs)
+    return round(d[len(d) // 2], 2) if d else None
+
+
 def timed_region(torch, step, first, steps, only=None):
     """Run ``steps`` steps between two HIP events on the launch stream (torch's
     current stream); returns (wall seconds, event seconds, launch counts)."""
@@ -819,6 +856,11 @@ def main():
     launches = {k: {"count": n, "avg_us": 1e6 * t,
                     "achieved_GBps": launch_bytes[k] / t / 1e9}
                 for k, (n, t) in per_label_s.items()}
+    # Supplementary: the median of 21 launches of each kind, each bracketed by
+    # its own events (includes the events' own overhead).
+    for k in launches:
+        launches[k]["median_us_event_per_launch"] = median_launch_us(
+            torch, step, args.warmup + args.steps, k)
     gpu_step_s = region_s / args.steps
     wall_step_s = elapsed / args.steps
     dom = launches[dominant]
@@ -826,6 +868,7 @@ def main():
             "unit": "GB/s", "frac": round(dom["achieved_GBps"] / PEAK_GBS, 4),
             "traffic": traffic_for(f"{TRAFFIC_SAME_AS.get(args.workload, args.workload)}:{dominant}"),
             "kernel": dominant, "avg_launch_us": round(dom["avg_us"], 2),
+            "median_launch_us_event_per_launch": dom["median_us_event_per_launch"],
             "algorithmic_bytes_per_launch": launch_bytes[dominant]}
 
     out = {
