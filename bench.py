@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Workloads whose dominant launches are exactly another workload's (same
 # kernel, same bytes per launch) share its counter measurement.
-TRAFFIC_SAME_AS = {"gpt2-small-all-ranks": "gpt2-small"}
+TRAFFIC_SAME_AS = {}
 
 
 def traffic_for(kernel_key):
@@ -158,18 +158,27 @@ def setup_gpt2(torch, zr, workloads, all_ranks=False):
         return cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R)
 
     if all_ranks:
-        # Every rank's partition in one step: the 8 fused launches back to
-        # back (each launch carries one partition's Adam state), 5.23 GB.
+        # Every rank's partition in one fused launch (dst = -1): the Adam
+        # state spans the whole padded flat space, partition k from k*P;
+        # 5.23 GB per step.
+        del states
+        L = R * P
+        master = torch.empty(L, device="cuda")
+        for k in range(R):
+            workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                    w.master_sigma, "cuda", out=master[k * P:(k + 1) * P])
+        master[T:] = 0.0
+        m, v = torch.zeros_like(master), torch.zeros_like(master)
+        pbf16 = torch.empty(L, dtype=torch.bfloat16, device="cuda")
+
         def step_all(i, timer):
-            for k in range(R):
-                s = states[k]
-                timer.launch(lambda: zr.zr_reduce_scatter_adam(
-                    plan, 0, -1, k, reps, s["master"], s["m"], s["v"], s["pbf16"], None,
-                    step=i + 1, **HP), "fused")
+            timer.launch(lambda: zr.zr_reduce_scatter_adam(
+                plan, 0, -1, -1, reps, master, m, v, pbf16, None, step=i + 1, **HP), "fused")
 
         cfg.update(workload=name + "-all-ranks", bytes_per_step=R * bytes_per_step,
-                   share="all 8 ranks' partitions per step, one fused launch each")
-        return step_all, R * bytes_per_step, R * P, cfg, launch_bytes, "fused", None
+                   share="all 8 ranks' partitions in one fused launch per step")
+        return step_all, R * bytes_per_step, R * P, cfg, {"fused": R * bytes_per_step}, \
+            "fused", None
     return step, bytes_per_step, P, cfg, launch_bytes, "fused", cpu_leg
 
 

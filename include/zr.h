@@ -242,8 +242,12 @@ zr_status zr_adam_partition(const zr_adam* h, const float* grad, float* master,
  * in a register and feeds Adam.  Bit-identical to the two calls in sequence.
  * Only the elements of the selected slices (plus the padding when the call
  * covers the last bucket, updated with a zero gradient) are updated.
- * dst >= 0; master, m, v (and param_bf16, grad_out when not null) are that
- * partition's P_g-element buffers; grad_out receives the reduced gradient. */
+ * dst >= 0: master, m, v (and param_bf16, grad_out when not null) are that
+ * partition's P_g-element buffers.  dst == -1: every rank's step in one
+ * launch; the buffers hold all R_g partitions back to back (L_g = R_g*P_g
+ * elements, partition d from element d*P_g), i.e. the group's whole padded
+ * flat space.  grad_out receives the reduced gradient.  Each partition's
+ * result is the same, bit for bit, as its own call with dst = d. */
 zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
                                  int64_t bucket, int32_t dst,
                                  const zr_replica* reps, zr_dtype grad_dtype,

@@ -62,8 +62,8 @@ int main(void) {
          zr_reduce_scatter_local(plan, 0, -1, -1, reps, (zr_dtype)7, outs, NULL),
          ZR_ERR_INVALID, NULL);
   zr_adam h = {1e-3, 0.9, 0.999, 1e-8, 1};
-  expect("fused: every destination at once",
-         zr_reduce_scatter_adam(plan, 0, -1, -1, reps, ZR_FP32, &h, outs[0], outs[1], outs[2],
+  expect("fused: dst past the last partition",
+         zr_reduce_scatter_adam(plan, 0, -1, 4, reps, ZR_FP32, &h, outs[0], outs[1], outs[2],
                                 NULL, NULL, NULL),
          ZR_ERR_INVALID, "dst");
   h.step = 0;

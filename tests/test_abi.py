@@ -105,12 +105,15 @@ def test_reduce_rejects_misaligned_and_null():
         zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, [_FakeTensor(0x100000, 570)] * 4, stream=0)
 
 
-def test_fused_needs_one_dst_and_valid_adam():
+def test_fused_checks_dst_state_sizes_and_adam():
     plan = _tiny_plan()
     reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
     buf = _FakeTensor(0x100000, 570)
-    with pytest.raises(zr.ZrError, match="one dst"):
+    # dst = -1 updates every partition: the state spans L = 2280 elements
+    with pytest.raises(zr.ZrError, match="touches 2280"):
         zr.zr_reduce_scatter_adam(plan, 0, -1, -1, reps, buf, buf, buf, stream=0)
+    with pytest.raises(zr.ZrError, match="dst"):
+        zr.zr_reduce_scatter_adam(plan, 0, -1, 4, reps, buf, buf, buf, stream=0)
     with pytest.raises(zr.ZrError, match="step"):
         zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, buf, buf, buf, step=0, stream=0)
     with pytest.raises(zr.ZrError, match="betas"):

@@ -199,6 +199,53 @@ def test_fused_equals_unfused_and_oracle(seed, is_bf16):
             assert (host_f32(fth)[first:] == 0).all()
 
 
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("is_bf16", [False, True])
+@pytest.mark.parametrize("per_bucket", [False, True])
+def test_fused_every_partition_in_one_call(seed, is_bf16, per_bucket):
+    """dst = -1 with state buffers over the whole padded flat space: one
+    launch (or one per bucket) updates every partition; each partition equals
+    the oracle and, bit for bit, its own single-partition call."""
+    numels, pg, groups, B, align = _make_case(200 + seed)
+    ref = plan_oracle(numels, pg, groups, B, align)
+    plan = zr.zr_plan_buckets(numels, pg, groups, B, 0, align)
+    rng = np.random.default_rng(50 + seed)
+    off = seed % 2
+    for g, info in enumerate(ref.groups):
+        if info.total == 0:
+            continue
+        P, R, L = info.part_numel, info.world, info.padded
+        reps = [_draw(rng, info.total, is_bf16, sigma=1e-3) for _ in range(R)]
+        dreps = [to_dev(x) for x in reps]
+        want_g = reduce_scatter_oracle(ref, g, reps, is_bf16)
+        th = (rng.standard_normal(L) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(L) * 1e-4).astype(np.float32)
+        v = np.abs(rng.standard_normal(L) * 1e-8).astype(np.float32)
+        th[info.total:] = m[info.total:] = v[info.total:] = 0.0
+        ath, am, av = to_dev(th, off), to_dev(m, off), to_dev(v, off)
+        apb = torch.zeros(L + 8, dtype=torch.bfloat16, device="cuda")[off: off + L]
+        ago = empty_f32(L, off)
+        for b in (range(ref.num_buckets) if per_bucket else [-1]):
+            zr.zr_reduce_scatter_adam(plan, g, b, -1, dreps, ath, am, av, apb, ago, step=2, **HP)
+        got = [host_f32(t) for t in (ago, ath, am, av)] + [host_u16(apb)]
+        for k in range(R):
+            sl = slice(k * P, (k + 1) * P)
+            kth, km, kv = to_dev(th[sl]), to_dev(m[sl]), to_dev(v[sl])
+            kpb = torch.zeros(P, dtype=torch.bfloat16, device="cuda")
+            kgo = empty_f32(P)
+            zr.zr_reduce_scatter_adam(plan, g, -1, k, dreps, kth, km, kv, kpb, kgo, step=2, **HP)
+            one = [host_f32(t) for t in (kgo, kth, km, kv)] + [host_u16(kpb)]
+            for a_, b_, nm in zip(got, one, ("grad", "master", "m", "v", "bf16")):
+                assert np.array_equal(a_[sl].view(np.uint8), b_.view(np.uint8)), \
+                    f"{nm} of partition {k}: every-partition call vs its own call"
+            assert_bits_equal(got[0][sl], want_g[k], f"grad of partition {k} vs oracle")
+            w_th, w_m, w_v = adam_oracle(want_g[k], th[sl], m[sl], v[sl], step=2, **HP)
+            assert_within(got[1][sl], w_th, what=f"master of partition {k}")
+            assert_within(got[2][sl], w_m, what=f"m of partition {k}")
+            assert_within(got[3][sl], w_v, atol=0.0, what=f"v of partition {k}")
+            assert np.array_equal(got[4][sl], bf16_rne_oracle(got[1][sl]))
+
+
 # Element offsets of (replicas, master / m / v / reduced-grad outputs, bf16
 # param) inside their allocations.  Each nonzero choice gives the first
 # segment of some partition a nonzero tile phase (replica tiles moved onto

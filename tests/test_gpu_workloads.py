@@ -93,6 +93,38 @@ def test_gpt2_small_fused_every_rank():
     _free()
 
 
+def test_gpt2_small_every_partition_in_one_call():
+    """All eight ranks' fused steps as one launch (dst = -1, state buffers over
+    the whole padded flat space), sampled per partition against the oracle."""
+    name = "gpt2-small"
+    w = workloads.get(name)
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    info = ref.groups[0]
+    T, P, R, L = info.total, info.part_numel, info.world, info.padded
+    reps = [workloads.device_normal(workloads.seed_for(name, r), T, w.grad_sigma, DEV, "bf16")
+            for r in range(R)]
+    master = torch.empty(L, device=DEV)
+    for k in range(R):
+        workloads.device_normal(workloads.seed_for(name, k, master=True), P, w.master_sigma,
+                                DEV, out=master[k * P:(k + 1) * P])
+    master[T:] = 0.0
+    idxs = [_sample(P, 20000, 30 + k, [s for s in ref.slices if s.dst == k]) for k in range(R)]
+    th_s = [_gather(master[k * P:(k + 1) * P], idxs[k]) for k in range(R)]
+    m, v = torch.zeros(L, device=DEV), torch.zeros(L, device=DEV)
+    pbf16 = torch.empty(L, dtype=torch.bfloat16, device=DEV)
+    gout = torch.empty(L, device=DEV)
+    zr.zr_reduce_scatter_adam(plan, 0, -1, -1, reps, master, m, v, pbf16, gout, **HP)
+    for k in range(R):
+        sl = slice(k * P, (k + 1) * P)
+        reps_s = [_gather(r_, k * P + idxs[k]) for r_ in reps]
+        _check_fused(reps_s, True, info.divisor, th_s[k], master[sl], m[sl], v[sl],
+                     pbf16[sl], gout[sl], idxs[k])
+        print(f"gpt2-small one call, partition {k}: {idxs[k].size} sampled elements ok")
+    del reps, master, m, v, pbf16, gout
+    _free()
+
+
 def test_llama3_8b_ipg_then_fused_rank_windows():
     name = "llama3-8b"
     w = workloads.get(name)

@@ -281,7 +281,9 @@ struct RedArgs {
   int32_t R;
   float divisor;
   float inv_divisor;
-  // fused mode: the one destination partition's buffers
+  // fused mode: the state buffers.  Partition d's element j sits at index
+  // d*state_stride + j (state_stride 0: the buffers hold one partition).
+  int64_t state_stride;
   float* master;
   float* m;
   float* v;
@@ -408,6 +410,9 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
     const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
+    // First element of the segment in the output or state buffers.
+    const int64_t spart =
+        kFused ? sg.part + static_cast<int64_t>(sg.dst) * a.state_stride : sg.part;
 
     // Every stream is slot-aligned at segment offset j (VE elements of 4 or
     // 2 bytes land on one 16- or 8-byte access).
@@ -417,14 +422,14 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         for (int r = 0; r < rr; ++r)
           ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT),
                              VE * sizeof(InT));
-      const uint64_t p4 = static_cast<uint64_t>(sg.part + j) * 4;
+      const uint64_t p4 = static_cast<uint64_t>(spart + j) * 4;
       if constexpr (kFused) {
         ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.m) + p4, 16) &&
              aligned(reinterpret_cast<uint64_t>(a.v) + p4, 16);
         if (a.pbf16)
           ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) +
-                                 static_cast<uint64_t>(sg.part + j) * 2, 8);
+                                 static_cast<uint64_t>(spart + j) * 2, 8);
         if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, 16);
       } else {
         ok = ok && aligned(a.out[sg.dst] + p4, 16);
@@ -455,14 +460,14 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     const int64_t rel0 = lt * kTileElems - shift;
 
     // Per-tile stream bases: element rel0 of the segment in every stream.
-    // sg.part + rel0 (and sg.flat + rel0) can be negative for a segment's
+    // spart + rel0 (and sg.flat + rel0) can be negative for a segment's
     // first tile; the byte offsets are formed by multiplying the signed
     // element offset, so they wrap modulo 2^64 and every lane's address
     // (base + its non-negative slot offset) comes out exact.  Never derive
     // one from another by division.
     const uint64_t in_off = static_cast<uint64_t>(sg.flat + rel0) * sizeof(InT);
-    const uint64_t p4 = static_cast<uint64_t>(sg.part + rel0) * 4;
-    const uint64_t p2 = static_cast<uint64_t>(sg.part + rel0) * 2;
+    const uint64_t p4 = static_cast<uint64_t>(spart + rel0) * 4;
+    const uint64_t p2 = static_cast<uint64_t>(spart + rel0) * 2;
     uint64_t b_master = 0, b_m = 0, b_v = 0, b_pb = 0, b_go = 0, b_out = 0;
     if constexpr (kFused) {
       b_master = reinterpret_cast<uint64_t>(a.master) + p4;
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
         for (int64_t e = e0; e < e1; ++e) {
           const float g = sg.pad ? 0.0f : reduce_one<InT, R, kDiv>(a, rr, sg.flat + e);
-          const int64_t j = sg.part + e;
+          const int64_t j = spart + e;
           if constexpr (!kFused) {
             reinterpret_cast<float*>(a.out[sg.dst])[j] = g;
           } else {
@@ -1120,7 +1125,6 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
     return fail(ZR_ERR_INVALID, "bucket index out of range");
   const zr::GroupInfo& gi = plan->groups[group];
   if (dst < -1 || dst >= gi.world) return fail(ZR_ERR_INVALID, "dst out of range");
-  if (fused && dst < 0) return fail(ZR_ERR_INVALID, "the fused step needs one dst");
   if (!reps) return fail(ZR_ERR_INVALID, "replicas are null");
   if (!valid_dtype(dt)) return fail(ZR_ERR_INVALID, "unsupported gradient dtype");
   const size_t s = dtype_size(dt);
@@ -1147,6 +1151,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
     a.pbf16 = pbf16;
     a.gout = gout;
     a.ac = ac;
+    a.state_stride = dst < 0 ? gi.part : 0;
   } else {
     if (!part_out) return fail(ZR_ERR_INVALID, "part_out is null");
     const int nout = dst < 0 ? gi.world : 1;

@@ -181,6 +181,15 @@ def _part_numel(plan, group):
     return P
 
 
+def _padded_numel(plan, group):
+    """L_g = R_g * P_g of the plan's group, queried once per plan and group."""
+    key = ("padded", group)
+    L = plan.part_numel.get(key)
+    if L is None:
+        L = plan.part_numel[key] = zr_plan_group_info(plan, group)[1]
+    return L
+
+
 def _dtype_code(t):
     dt = t.dtype
     if dt is torch.bfloat16:
@@ -384,7 +393,8 @@ def zr_reduce_scatter_adam(plan, group, bucket, dst, reps, master, m, v,
                            beta2=0.999, eps=1e-8, step=1, stream=None):
     arr, dt = _replicas(reps)
     h = _adam(lr, beta1, beta2, eps, step)
-    P = _part_numel(plan, group)
+    # dst == -1: the state buffers hold every partition (L_g elements)
+    P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
     _check(_lib.zr_reduce_scatter_adam(plan.handle, int(group), int(bucket),
                                        int(dst), arr, dt, ctypes.byref(h),
                                        _buf(master, "master", ZR_FP32, P),
