@@ -32,6 +32,9 @@
  *   - The library owns a plan (create with zr_plan_buckets, free with
  *     zr_plan_free).  A plan is immutable; small device tables derived from
  *     it are built on first use (a synchronous upload) and freed with it.
+ *     Each (group, bucket, dst, device) selection has its own table, so a
+ *     call recorded into a HIP graph must not be that selection's first:
+ *     make it once outside the capture (the upload allocates and copies).
  *   - Work is enqueued on the caller's HIP stream; nothing synchronises
  *     implicitly.  Completion is the caller's stream synchronisation.
  *   - Every call returns a zr_status.  Arguments are validated before any
