@@ -643,7 +643,7 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False):
            "reduce_bucket_size": w.reduce_bucket_size, "buckets": nb,
            "reduce_launches_per_step": len(pairs), "adam_launches_per_step": len(groups),
            "partition_elems": [gr["P"] for gr in groups], "grad_dtype": "fp32",
-           "bytes_per_step": total_bytes}
+           "bytes_per_step": total_bytes, "launch_sizes": "mixed"}
     if not graph:
         return (lambda i, timer: eager(i + 1, timer)), total_bytes, \
             sum(gr["P"] for gr in groups), cfg, launch_bytes, "reduce", None
@@ -661,6 +661,7 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False):
         eager(1, Timer())
     torch.cuda.synchronize()
     cfg["graph"] = "one captured step per replay (Adam step number fixed at capture)"
+    del cfg["launch_sizes"]                   # one replay per step
     return (lambda i, timer: timer.launch(cg.replay, "graph")), total_bytes, \
         sum(gr["P"] for gr in groups), cfg, {"graph": total_bytes}, "graph", None
 
@@ -866,10 +867,11 @@ def main():
                     "achieved_GBps": launch_bytes[k] / t / 1e9}
                 for k, (n, t) in per_label_s.items()}
     # Supplementary: the median of 21 launches of each kind, each bracketed by
-    # its own events (includes the events' own overhead).
+    # its own events (includes the events' own overhead).  Skipped where one
+    # kind of launch comes in several sizes (a median of those means nothing).
     for k in launches:
-        launches[k]["median_us_event_per_launch"] = median_launch_us(
-            torch, step, args.warmup + args.steps, k)
+        launches[k]["median_us_event_per_launch"] = None if cfg.get("launch_sizes") == \
+            "mixed" else median_launch_us(torch, step, args.warmup + args.steps, k)
     gpu_step_s = region_s / args.steps
     wall_step_s = elapsed / args.steps
     dom = launches[dominant]
