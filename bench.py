@@ -46,9 +46,10 @@ def traffic_for(kernel_key):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    from zero_partition_aware_amd.build import source_hash
+    from zero_partition_aware_amd.build import device_code_hash
     entry = t.get(kernel_key)
-    if not entry or entry.get("kernel_src_sha") != source_hash():
+    dev = device_code_hash()
+    if not entry or dev is None or entry.get("device_code_sha") != dev:
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -335,7 +336,14 @@ def run_overlap(torch, zr, workloads, args):
     rank's partition is launched on stream B after an event from stream A;
     the other 7 replicas' windows are resident.  Backward-only, reduce-only
     and serial times are taken on one stream; the overlapped run uses two.
-    Checks that the overlapped result equals the serial one bit for bit."""
+    Besides the plain two-stream run, each value of ``--reduce-cus`` splits
+    the compute units between the streams (CU-masked streams: the reduction
+    on that many, the backward on the rest), and each nonzero value of
+    ``--reduce-wgs`` caps the overlapped reductions' launches at that many
+    workgroups.  The hidden fraction, (serial - overlapped) / reduce-only, is
+    always measured against the unpartitioned, uncapped serial step and may
+    be negative.  Checks that every overlapped result equals the serial one
+    bit for bit."""
     name = "llama3-8b"
     w = workloads.get(name)
     order = list(range(len(w.numels)))[::-1]
@@ -347,21 +355,50 @@ def run_overlap(torch, zr, workloads, args):
     hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime torch already holds
     created = []
 
-    def new_stream():
+    def new_stream(cus=None):
         """A default-priority, non-blocking HIP stream created through the
         runtime torch holds (no torch stream pool), destroyed after each
-        configuration."""
+        configuration.  ``cus``: the compute units (bit indices of the
+        runtime's CU mask) the stream's kernels may use; None = all."""
         h = ctypes.c_void_p()
-        err = hip.hipStreamCreateWithFlags(ctypes.byref(h), ctypes.c_uint(1))
+        if cus is None:
+            err = hip.hipStreamCreateWithFlags(ctypes.byref(h), ctypes.c_uint(1))
+        else:
+            words = [0] * ((n_cus + 31) // 32)
+            for c in cus:
+                words[c // 32] |= 1 << (c % 32)
+            mask = (ctypes.c_uint32 * len(words))(*words)
+            err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(len(words)),
+                                                   mask)
         if err != 0:
             raise RuntimeError(f"stream creation failed with HIP error {err}")
         created.append(h)
         return torch.cuda.ExternalStream(h.value)
 
+    def destroy_stream(ext):
+        """Destroys one stream made by new_stream (CU-masked streams each
+        hold a hardware queue of their own, so they are not kept around)."""
+        torch.cuda.synchronize()
+        for i, h in enumerate(created):
+            if h.value == ext.cuda_stream:
+                hip.hipStreamDestroy(created.pop(i))
+                return
+
     def destroy_streams():
         torch.cuda.synchronize()
         while created:
             hip.hipStreamDestroy(created.pop())
+
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def reduce_cu_set(n):
+        """n compute units for the reduction stream: the lowest n bits of the
+        CU mask.  The runtime deals mask bits out to the 8 XCDs in turn, so
+        these are n/8 CUs on every XCD (a mask that leaves an XCD without CUs
+        cannot be given to a stream: every queue dispatches to every XCD)."""
+        if n % 8:
+            raise SystemExit("--reduce-cus values must be multiples of 8 (one CU per XCD)")
+        return list(range(n))
 
     o_max = max(s[0] for s in shapes if len(s) == 2)
     # Contiguous operands only (one activation matrix per input width).
@@ -375,7 +412,6 @@ def run_overlap(torch, zr, workloads, args):
     ref_master = None
     s_full = torch.cuda.current_stream()      # serial reference on every CU
     for B in args.buckets:
-        sa, sb = new_stream(), new_stream()
         plan = zr.zr_plan_buckets(numels, [0] * len(numels), [(R, 1)], B)
         T, L, P, D = zr.zr_plan_group_info(plan, 0)
         nb = zr.zr_plan_num_buckets(plan)
@@ -400,9 +436,14 @@ def run_overlap(torch, zr, workloads, args):
             state["pb"] = torch.empty(P, dtype=torch.bfloat16, device=dev)
             torch.cuda.synchronize()
 
-        def reduce_bucket(b):
-            zr.zr_reduce_scatter_adam(plan, 0, b, k, reps, state["master"], state["m"],
-                                      state["v"], state["pb"], None, **HP)
+        def reduce_bucket(b, cap=0):
+            if cap:
+                zr.zr_reduce_scatter_adam_capped(plan, 0, b, k, reps, state["master"],
+                                                 state["m"], state["v"], state["pb"], None,
+                                                 max_workgroups=cap, **HP)
+            else:
+                zr.zr_reduce_scatter_adam(plan, 0, b, k, reps, state["master"], state["m"],
+                                          state["v"], state["pb"], None, **HP)
 
         def backward(on_bucket):
             done = 0
@@ -431,47 +472,72 @@ def run_overlap(torch, zr, workloads, args):
                 for b in range(nb):
                     reduce_bucket(b)
 
-        def run_overlap_once():
+        def run_overlap_once(cap, sa, sb):
             def on_bucket(b):
                 ev = torch.cuda.Event()
                 ev.record(sa)
                 sb.wait_event(ev)
                 with torch.cuda.stream(sb):
-                    reduce_bucket(b)
+                    reduce_bucket(b, cap)
             with torch.cuda.stream(sa):
                 backward(on_bucket)
             sa.wait_stream(sb)
 
-        def run_backward():
-            with torch.cuda.stream(s_full):
+        def run_backward(stream=s_full):
+            with torch.cuda.stream(stream):
                 backward(lambda b: None)
 
-        def run_reduce():
-            with torch.cuda.stream(s_full):
+        def run_reduce(cap=0, stream=s_full):
+            with torch.cuda.stream(stream):
                 for b in range(nb):
-                    reduce_bucket(b)
+                    reduce_bucket(b, cap)
 
         reset(); run_serial(); torch.cuda.synchronize()       # warm-up
         reset(); t_bwd = timed(run_backward)
         t_red = timed(run_reduce)
         reset(); t_ser = timed(run_serial)
         serial_master = state["master"].clone()
-        reset(); run_overlap_once(); torch.cuda.synchronize()
-        reset(); t_ovl = timed(run_overlap_once)
-        same = bool(torch.equal(serial_master.view(torch.int32), state["master"].view(torch.int32)))
         if ref_master is None:
             ref_master = serial_master
         same_across_b = bool(torch.equal(ref_master.view(torch.int32),
                                          serial_master.view(torch.int32)))
-        results[f"B={B}"] = {"reduce_bucket_size": B,
-                           "buckets": nb, "t_backward_ms": 1e3 * t_bwd,
-                           "t_reduce_ms": 1e3 * t_red, "t_serial_ms": 1e3 * t_ser,
-                           "t_overlap_ms": 1e3 * t_ovl,
-                           "hidden_fraction": max(0.0, (t_ser - t_ovl) / t_red),
-                           "overlap_bitwise_equal_serial": same,
-                           "equal_across_bucket_sizes": same_across_b}
-        print(f"overlap B={B}: {nb} buckets, serial {1e3 * t_ser:.1f} ms, "
-              f"overlapped {1e3 * t_ovl:.1f} ms, equal {same}", file=sys.stderr, flush=True)
+        # Configurations: CU-partitioned streams (reduction on ncu compute
+        # units, backward on the rest) and grid caps on unpartitioned streams.
+        configs = ([(ncu, 0) for ncu in args.reduce_cus] +
+                   [(0, cap) for cap in args.reduce_wgs if cap])
+        for ncu, cap in configs:
+            # One pair of streams per configuration, destroyed after it: a
+            # CU-masked stream holds a hardware queue of its own, and a
+            # process has few.
+            if ncu:
+                red_set = reduce_cu_set(ncu)
+                rest = sorted(set(range(n_cus)) - set(red_set))
+                xa, xb = new_stream(rest), new_stream(red_set)
+            else:
+                xa, xb = new_stream(), new_stream()
+            t_bwd_cfg = t_bwd if ncu == 0 else timed(lambda: run_backward(xa))
+            t_red_cfg = (t_red if (ncu, cap) == (0, 0)
+                         else timed(lambda: run_reduce(cap, xb)))
+            reset(); run_overlap_once(cap, xa, xb); torch.cuda.synchronize()
+            reset(); t_ovl = timed(lambda: run_overlap_once(cap, xa, xb))
+            same = bool(torch.equal(serial_master.view(torch.int32),
+                                    state["master"].view(torch.int32)))
+            results[f"B={B},cus={ncu},wgs={cap}"] = {
+                "reduce_bucket_size": B, "buckets": nb, "reduce_cus": ncu,
+                "reduce_max_workgroups": cap,
+                "t_backward_ms": 1e3 * t_bwd, "t_backward_this_config_ms": 1e3 * t_bwd_cfg,
+                "t_reduce_ms": 1e3 * t_red, "t_reduce_this_config_ms": 1e3 * t_red_cfg,
+                "t_serial_ms": 1e3 * t_ser, "t_overlap_ms": 1e3 * t_ovl,
+                "hidden_fraction": (t_ser - t_ovl) / t_red,
+                "overlap_bitwise_equal_serial": same,
+                "equal_across_bucket_sizes": same_across_b}
+            print(f"overlap B={B} cus={ncu} wgs={cap}: {nb} buckets, backward "
+                  f"{1e3 * t_bwd:.1f} ms (this config {1e3 * t_bwd_cfg:.1f}), reduce "
+                  f"{1e3 * t_red:.1f} ms (this config {1e3 * t_red_cfg:.1f}), serial "
+                  f"{1e3 * t_ser:.1f} ms, overlapped {1e3 * t_ovl:.1f} ms, hidden "
+                  f"{(t_ser - t_ovl) / t_red:.3f}, equal {same}", file=sys.stderr, flush=True)
+            destroy_stream(xa)
+            destroy_stream(xb)
         del mg, others, reps, master0, state
         destroy_streams()
         torch.cuda.empty_cache()
@@ -814,6 +880,14 @@ def main():
                          "plus IPG fills, or IPG fills alone")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="tokens of the backward GEMM stand-in (llama3-8b-overlap)")
+    ap.add_argument("--reduce-wgs", type=lambda t: [int(x) for x in t.split(",")],
+                    default=[0],
+                    help="workgroup caps of the overlapped reductions, each run on "
+                         "unpartitioned streams (llama3-8b-overlap; 0 = none)")
+    ap.add_argument("--reduce-cus", type=lambda t: [int(x) for x in t.split(",")],
+                    default=[0],
+                    help="compute units given to the reduction stream, the rest to the "
+                         "backward stream (llama3-8b-overlap; 0 = no partition)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

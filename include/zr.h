@@ -258,6 +258,25 @@ zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
                                  float* v, uint16_t* param_bf16,
                                  float* grad_out, hipStream_t stream);
 
+/* zr_reduce_scatter_adam_capped -- zr_reduce_scatter_adam on a launch of at
+ * most max_workgroups workgroups (>= 1; ZR_ERR_INVALID otherwise), each
+ * walking the selection's tiles in steps of the grid.  For a reduction that
+ * overlaps the backward pass on a second stream ([ZeRO-RS blog] §四: each
+ * IPG bucket is reduced as soon as it is full, while backward continues;
+ * [Megatron DP] "梯度缓冲区+分桶+overlap"): the cap bounds the workgroup
+ * slots the reduction holds at once, leaving the rest to the backward's
+ * kernels; with one tile in flight per workgroup, the HBM-bound reduction
+ * slows as the cap shrinks.  Results are bit-identical to
+ * zr_reduce_scatter_adam for every cap (the same per-element code); only the
+ * launch shape differs.  Errors as zr_reduce_scatter_adam. */
+zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t group,
+                                        int64_t bucket, int32_t dst,
+                                        const zr_replica* reps, zr_dtype grad_dtype,
+                                        const zr_adam* h, float* master, float* m,
+                                        float* v, uint16_t* param_bf16,
+                                        float* grad_out, int32_t max_workgroups,
+                                        hipStream_t stream);
+
 /* zr_ring_rs_step -- one step of ring reduce-scatter with every card's buffer
  * resident in this GPU ([Megatron DP] "深入：all-reduce 底层算法（NCCL）", ring
  * reduce-scatter phase).  rank_bufs[n_ranks] (host array of device fp32

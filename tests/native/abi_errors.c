@@ -72,6 +72,14 @@ int main(void) {
                                 NULL, NULL, NULL),
          ZR_ERR_INVALID, "step");
   h.step = 1;
+  expect("capped fused: no workgroups",
+         zr_reduce_scatter_adam_capped(plan, 0, -1, 0, reps, ZR_FP32, &h, outs[0], outs[1],
+                                       outs[2], NULL, NULL, 0, NULL),
+         ZR_ERR_INVALID, "max_workgroups");
+  expect("capped fused: dst past the last partition",
+         zr_reduce_scatter_adam_capped(plan, 0, -1, 4, reps, ZR_FP32, &h, outs[0], outs[1],
+                                       outs[2], NULL, NULL, 64, NULL),
+         ZR_ERR_INVALID, "dst");
   expect("adam: negative n",
          zr_adam_partition(&h, outs[0], outs[1], outs[2], outs[3], NULL, -1, NULL),
          ZR_ERR_INVALID, "n must");

@@ -120,6 +120,23 @@ def test_fused_checks_dst_state_sizes_and_adam():
         zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, buf, buf, buf, beta1=1.0, stream=0)
 
 
+def test_capped_fused_checks_the_cap_then_the_fused_arguments():
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    for cap in (0, -3):
+        with pytest.raises(zr.ZrError, match="max_workgroups") as ei:
+            zr.zr_reduce_scatter_adam_capped(plan, 0, -1, 0, reps, buf, buf, buf,
+                                             max_workgroups=cap, stream=0)
+        assert ei.value.status == zr.ZR_ERR_INVALID
+    with pytest.raises(zr.ZrError, match="dst"):
+        zr.zr_reduce_scatter_adam_capped(plan, 0, -1, 4, reps, buf, buf, buf,
+                                         max_workgroups=8, stream=0)
+    with pytest.raises(zr.ZrError, match="step"):
+        zr.zr_reduce_scatter_adam_capped(plan, 0, -1, 0, reps, buf, buf, buf, step=0,
+                                         max_workgroups=8, stream=0)
+
+
 def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
     plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
     g = _FakeTensor(0x1000, 10, "bf16")

@@ -33,28 +33,48 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _code_text(path):
-    """A C/C++ source with its comments removed and whitespace collapsed: the
-    part of the file that reaches the compiler."""
-    import re
-    with open(path) as fh:
-        text = fh.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return " ".join(text.split())
+# The device code's fingerprint: a hash of the gfx950 code object's
+# instructions (.text), kernel descriptors (.rodata) and kernel metadata
+# (.note), written beside the library at build time.  The rest of the ELF
+# (build ids, symbol tables) differs from compile to compile, and host-side
+# edits leave these sections alone, so counter measurements stay tied to the
+# exact kernels they were taken on.
+DEVICE_SHA = os.path.join(HERE, "libzr.device_sha")
+DEVICE_SECTIONS = (".text", ".rodata", ".note")
 
 
-def source_hash():
-    """Short hash of the device code and its compile flags (comments and
-    whitespace excluded): counter measurements are only valid for the exact
-    code they were taken on."""
+def _objcopy():
+    for cand in ("/opt/rocm/llvm/bin/llvm-objcopy", shutil.which("llvm-objcopy")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("llvm-objcopy not found: the ROCm LLVM tools are required")
+
+
+def _device_code_hash(hipcc):
     import hashlib
-    h = hashlib.sha256()
-    for path in (os.path.join(CSRC, "zr_kernels.hip"), os.path.join(CSRC, "zr_internal.h"),
-                 os.path.join(INCLUDE, "zr.h")):
-        h.update(_code_text(path).encode())
-    h.update(" ".join(HIP_FLAGS).encode())
-    return h.hexdigest()[:16]
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        obj = os.path.join(tmp, "dev.o")
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "--cuda-device-only",
+              "--no-gpu-bundle-output", "-c", os.path.join(CSRC, "zr_kernels.hip"),
+              "-o", obj])
+        h = hashlib.sha256()
+        for sec in DEVICE_SECTIONS:
+            out = os.path.join(tmp, "sec.bin")
+            _run([_objcopy(), "--dump-section", f"{sec}={out}", obj])
+            with open(out, "rb") as fh:
+                data = fh.read()
+            h.update(sec.encode() + len(data).to_bytes(8, "little") + data)
+        return h.hexdigest()[:16]
+
+
+def device_code_hash():
+    """Fingerprint of the built library's device code (None if not built)."""
+    try:
+        with open(DEVICE_SHA) as fh:
+            return fh.read().strip() or None
+    except OSError:
+        return None
 
 
 def _run(cmd):
@@ -86,6 +106,8 @@ def build(verbose=False):
                  "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
                  "-Wl,--no-undefined", "-o", tmp])
     os.replace(tmp, LIB)
+    with open(DEVICE_SHA, "w") as fh:
+        fh.write(_device_code_hash(hipcc) + "\n")
     if verbose:
         print(out)
     return LIB

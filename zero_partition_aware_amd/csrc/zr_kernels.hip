@@ -1112,11 +1112,13 @@ zr_status launch_reduce_t(const RedArgs& a, int R, bool div, unsigned grid, hipS
   return check_launch(kFused ? "reduce_scatter_adam launch" : "reduce_scatter launch");
 }
 
-// Shared validation + launch of the reduce kernel in either mode.
+// Shared validation + launch of the reduce kernel in either mode; max_wgs > 0
+// caps the grid (0: one workgroup per tile).
 zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t dst,
                      const zr_replica* reps, zr_dtype dt, float* const* part_out,
                      const zr_adam* h, float* master, float* m, float* v,
-                     uint16_t* pbf16, float* gout, bool fused, hipStream_t stream) {
+                     uint16_t* pbf16, float* gout, bool fused, int64_t max_wgs,
+                     hipStream_t stream) {
   zr::clear_error();
   if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
   if (group < 0 || group >= static_cast<int32_t>(plan->groups.size()))
@@ -1192,7 +1194,11 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   a.divisor = static_cast<float>(gi.divisor);
   a.inv_divisor = 1.0f / static_cast<float>(gi.divisor);
   const bool div = !pow2(gi.divisor);
-  const unsigned grid = grid_for(a.total_tiles, cus);
+  // A capped grid walks the tiles in steps of its size (the kernel's
+  // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
+  const unsigned grid = max_wgs > 0
+      ? static_cast<unsigned>(std::min<int64_t>(grid_for(a.total_tiles, cus), max_wgs))
+      : grid_for(a.total_tiles, cus);
   if (dt == ZR_BF16)
     return fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, grid, stream)
                  : launch_reduce_t<uint16_t, false>(a, gi.world, div, grid, stream);
@@ -1210,7 +1216,7 @@ extern "C" zr_status zr_reduce_scatter_local(const zr_plan* plan, int32_t group,
                                              float* const* part_out, hipStream_t stream) {
   try {
     return run_reduce(plan, group, bucket, dst, reps, grad_dtype, part_out, nullptr,
-                      nullptr, nullptr, nullptr, nullptr, nullptr, false, stream);
+                      nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, stream);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1224,7 +1230,27 @@ extern "C" zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
                                             float* grad_out, hipStream_t stream) {
   try {
     return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
-                      v, param_bf16, grad_out, true, stream);
+                      v, param_bf16, grad_out, true, 0, stream);
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
+
+extern "C" zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t group,
+                                                   int64_t bucket, int32_t dst,
+                                                   const zr_replica* reps,
+                                                   zr_dtype grad_dtype, const zr_adam* h,
+                                                   float* master, float* m, float* v,
+                                                   uint16_t* param_bf16, float* grad_out,
+                                                   int32_t max_workgroups,
+                                                   hipStream_t stream) {
+  try {
+    if (max_workgroups < 1) {
+      zr::clear_error();
+      return fail(ZR_ERR_INVALID, "max_workgroups must be >= 1");
+    }
+    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
+                      v, param_bf16, grad_out, true, max_workgroups, stream);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }

@@ -18,7 +18,7 @@ import os
 import shlex
 import sys
 
-from .build import source_hash
+from .build import device_code_hash
 
 
 def _avg_kib(path, match):
@@ -52,7 +52,10 @@ def main():
     w_scale = args.copy_bytes / (cw_kib * 1024)
     read_b = f_kib * 1024 * f_scale
     write_b = w_kib * 1024 * w_scale
-    entry = {"kernel_src_sha": source_hash(),
+    dev = device_code_hash()
+    if dev is None:
+        raise SystemExit("libzr is not built: no device code fingerprint to key the entry to")
+    entry = {"device_code_sha": dev,
              "hbm_bytes_per_launch": round(read_b + write_b),
              "read_bytes_per_launch": round(read_b),
              "write_bytes_per_launch": round(write_b),
