@@ -137,6 +137,31 @@ def test_capped_fused_checks_the_cap_then_the_fused_arguments():
                                          max_workgroups=8, stream=0)
 
 
+def test_binding_rejects_integers_ctypes_would_wrap():
+    """ctypes passes 2**32 + 5 to an int32_t as 5; the binding refuses it
+    instead of selecting another partition or bucket."""
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    for kwargs, name in ((dict(dst=2 ** 32), "dst"), (dict(group=-(2 ** 31) - 1), "group"),
+                         (dict(bucket=2 ** 63), "bucket"), (dict(step=2 ** 64 + 1), "step")):
+        args = dict(group=0, bucket=-1, dst=0, step=1)
+        args.update(kwargs)
+        with pytest.raises(zr.ZrError, match=name) as ei:
+            zr.zr_reduce_scatter_adam(plan, args["group"], args["bucket"], args["dst"], reps,
+                                      buf, buf, buf, step=args["step"], stream=0)
+        assert ei.value.status == zr.ZR_ERR_INVALID
+    with pytest.raises(zr.ZrError, match="max_workgroups"):
+        zr.zr_reduce_scatter_adam_capped(plan, 0, -1, 0, reps, buf, buf, buf,
+                                         max_workgroups=2 ** 32 + 5, stream=0)
+    with pytest.raises(zr.ZrError, match="numels"):
+        zr.zr_plan_buckets([2 ** 63], [0], [(4, 1)], 1000)
+    with pytest.raises(zr.ZrError, match="integer"):
+        zr.zr_plan_grad_start_offset(plan, 1, 1.5)
+    # integral floats keep working (bucket sizes are often written 5e8)
+    assert zr.zr_plan_num_buckets(zr.zr_plan_buckets([10, 20], [0, 0], [(2, 1)], 1e1)) == 3
+
+
 def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
     plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
     g = _FakeTensor(0x1000, 10, "bf16")

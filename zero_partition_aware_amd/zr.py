@@ -8,6 +8,7 @@ fallback: if the library is missing the import fails.
 """
 
 import ctypes
+import operator
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -143,6 +144,31 @@ def zr_version():
 
 # ------------------------------------------------------------ marshalling
 
+def _int(x, bits, name):
+    """A Python integer for a C int32_t / int64_t argument.  ctypes wraps
+    out-of-range values silently (2**32 + 5 would arrive as 5), so the range
+    is checked here and a violation raises ZrError(ZR_ERR_INVALID)."""
+    if isinstance(x, float) and x.is_integer():
+        v = int(x)                      # e.g. reduce_bucket_size=5e8
+    else:
+        try:
+            v = operator.index(x)
+        except TypeError:
+            raise ZrError(ZR_ERR_INVALID, f"{name} must be an integer, not {x!r}") from None
+    lim = 1 << (bits - 1)
+    if not -lim <= v < lim:
+        raise ZrError(ZR_ERR_INVALID, f"{name} = {v} does not fit in int{bits}_t")
+    return v
+
+
+def _i32(x, name):
+    return _int(x, 32, name)
+
+
+def _i64(x, name):
+    return _int(x, 64, name)
+
+
 def _ptr(t):
     """Device (or host) address of a tensor, or None for None."""
     if t is None:
@@ -212,7 +238,7 @@ def _stream(stream):
 
 
 def _adam(lr, beta1, beta2, eps, step):
-    return zr_adam(float(lr), float(beta1), float(beta2), float(eps), int(step))
+    return zr_adam(float(lr), float(beta1), float(beta2), float(eps), _i64(step, "step"))
 
 
 class Plan:
@@ -246,14 +272,15 @@ def zr_plan_buckets(numels, param_groups, groups, reduce_bucket_size,
     n = len(numels)
     params = (zr_param * max(n, 1))()
     for i, (ne, g) in enumerate(zip(numels, param_groups)):
-        params[i] = zr_param(int(ne), int(g))
+        params[i] = zr_param(_i64(ne, f"numels[{i}]"), _i32(g, f"param_groups[{i}]"))
     gs = (zr_group * max(len(groups), 1))()
     for i, (w, sp) in enumerate(groups):
-        gs[i] = zr_group(int(w), int(sp))
+        gs[i] = zr_group(_i32(w, f"groups[{i}].world"), _i32(sp, f"groups[{i}].sp"))
     out = c_vp()
-    _check(_lib.zr_plan_buckets(params, n, gs, len(groups),
-                                int(reduce_bucket_size),
-                                int(partition_gradients), int(align),
+    _check(_lib.zr_plan_buckets(params, n, gs, _i32(len(groups), "len(groups)"),
+                                _i64(reduce_bucket_size, "reduce_bucket_size"),
+                                _i32(partition_gradients, "partition_gradients"),
+                                _i64(align, "align"),
                                 ctypes.byref(out)))
     return Plan(out.value)
 
@@ -283,7 +310,7 @@ def zr_plan_partition_gradients(plan):
 def zr_plan_group_info(plan, g):
     """(total, padded, part_numel, divisor)."""
     t, L, P, d = c_i64(), c_i64(), c_i64(), ctypes.c_float()
-    _check(_lib.zr_plan_group_info(plan.handle, int(g), ctypes.byref(t),
+    _check(_lib.zr_plan_group_info(plan.handle, _i32(g, "group"), ctypes.byref(t),
                                    ctypes.byref(L), ctypes.byref(P),
                                    ctypes.byref(d)))
     return t.value, L.value, P.value, d.value
@@ -291,20 +318,20 @@ def zr_plan_group_info(plan, g):
 
 def zr_plan_param_offset(plan, p):
     v = c_i64()
-    _check(_lib.zr_plan_param_offset(plan.handle, int(p), ctypes.byref(v)))
+    _check(_lib.zr_plan_param_offset(plan.handle, _i64(p, "p"), ctypes.byref(v)))
     return v.value
 
 
 def zr_plan_param_partitions(plan, p):
     ids, n = _P(c_i32)(), c_i32()
-    _check(_lib.zr_plan_param_partitions(plan.handle, int(p), ctypes.byref(ids),
+    _check(_lib.zr_plan_param_partitions(plan.handle, _i64(p, "p"), ctypes.byref(ids),
                                          ctypes.byref(n)))
     return [ids[i] for i in range(n.value)]
 
 
 def zr_plan_grad_start_offset(plan, p, k):
     v = c_i64()
-    _check(_lib.zr_plan_grad_start_offset(plan.handle, int(p), int(k),
+    _check(_lib.zr_plan_grad_start_offset(plan.handle, _i64(p, "p"), _i32(k, "k"),
                                           ctypes.byref(v)))
     return v.value
 
@@ -312,7 +339,7 @@ def zr_plan_grad_start_offset(plan, p, k):
 def zr_plan_param_buckets(plan, p):
     """(first, last) bucket param p feeds."""
     a, b = c_i64(), c_i64()
-    _check(_lib.zr_plan_param_buckets(plan.handle, int(p), ctypes.byref(a), ctypes.byref(b)))
+    _check(_lib.zr_plan_param_buckets(plan.handle, _i64(p, "p"), ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
 
 
@@ -320,7 +347,7 @@ def zr_plan_slices(plan, bucket=-1):
     """List of slice tuples (bucket, group, dst, bucket_offset, flat_offset,
     part_offset, numel)."""
     s, n = _P(zr_slice)(), c_i64()
-    _check(_lib.zr_plan_slices(plan.handle, int(bucket), ctypes.byref(s),
+    _check(_lib.zr_plan_slices(plan.handle, _i64(bucket, "bucket"), ctypes.byref(s),
                                ctypes.byref(n)))
     return [s[i].astuple() for i in range(n.value)]
 
@@ -332,13 +359,13 @@ def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
     n = len(param_ids)
     if len(grads) != n:
         raise ZrError(ZR_ERR_INVALID, "param_ids and grads differ in length")
-    ids = (c_i64 * max(n, 1))(*[int(p) for p in param_ids])
+    ids = (c_i64 * max(n, 1))(*[_i64(p, f"param_ids[{i}]") for i, p in enumerate(param_ids)])
     dt = _dtype_code(grads[0]) if n else ZR_FP32
     ptrs = (c_vp * max(n, 1))(*[_buf(g, f"grads[{i}]", dt).value for i, g in enumerate(grads)])
-    wl = main_grad.numel() if window_len is None else int(window_len)
+    wl = main_grad.numel() if window_len is None else _i64(window_len, "window_len")
     _check(_lib.zr_ipg_accumulate(plan.handle, ids, ptrs, n, dt,
                                   _buf(main_grad, "main_grad", ZR_FP32, wl),
-                                  int(window_base), wl, _stream(stream)))
+                                  _i64(window_base, "window_base"), wl, _stream(stream)))
 
 
 def _replicas(reps):
@@ -348,7 +375,8 @@ def _replicas(reps):
     for i, r in enumerate(reps):
         t, base = (r, 0) if not isinstance(r, tuple) else r
         dt = _dtype_code(t) if dt is None else dt
-        arr[i] = zr_replica(_buf(t, f"replica {i}", dt).value, int(base), t.numel())
+        arr[i] = zr_replica(_buf(t, f"replica {i}", dt).value, _i64(base, f"replica {i} flat_base"),
+                            t.numel())
     return arr, (ZR_FP32 if dt is None else dt)
 
 
@@ -361,8 +389,8 @@ def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
     outs = (c_vp * max(len(part_out), 1))(
         *[_buf(t, f"part_out[{i}]", ZR_FP32, P).value if t is not None else None
           for i, t in enumerate(part_out)])
-    _check(_lib.zr_reduce_scatter_local(plan.handle, int(group), int(bucket),
-                                        int(dst), arr, dt, outs,
+    _check(_lib.zr_reduce_scatter_local(plan.handle, _i32(group, "group"),
+                                        _i64(bucket, "bucket"), _i32(dst, "dst"), arr, dt, outs,
                                         _stream(stream)))
 
 
@@ -374,7 +402,7 @@ def zr_copy_grads_in_partition(plan, group, bucket, dst, bucket_layout_src,
             if s[1] == int(group) and s[2] == int(dst):
                 need = max(need, s[3] + s[6])
     _check(_lib.zr_copy_grads_in_partition(
-        plan.handle, int(group), int(bucket), int(dst),
+        plan.handle, _i32(group, "group"), _i64(bucket, "bucket"), _i32(dst, "dst"),
         _buf(bucket_layout_src, "bucket_layout_src", ZR_FP32, need),
         _buf(part_out, "part_out", ZR_FP32, _part_numel(plan, group)), _stream(stream)))
 
@@ -382,7 +410,7 @@ def zr_copy_grads_in_partition(plan, group, bucket, dst, bucket_layout_src,
 def zr_adam_partition(grad, master, m, v, param_bf16=None, lr=1e-3, beta1=0.9,
                       beta2=0.999, eps=1e-8, step=1, n=None, stream=None):
     h = _adam(lr, beta1, beta2, eps, step)
-    nn = master.numel() if n is None else int(n)
+    nn = master.numel() if n is None else _i64(n, "n")
     need = max(nn, 0)
     _check(_lib.zr_adam_partition(ctypes.byref(h), _buf(grad, "grad", ZR_FP32, need),
                                   _buf(master, "master", ZR_FP32, need),
@@ -398,8 +426,9 @@ def zr_reduce_scatter_adam(plan, group, bucket, dst, reps, master, m, v,
     h = _adam(lr, beta1, beta2, eps, step)
     # dst == -1: the state buffers hold every partition (L_g elements)
     P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
-    _check(_lib.zr_reduce_scatter_adam(plan.handle, int(group), int(bucket),
-                                       int(dst), arr, dt, ctypes.byref(h),
+    _check(_lib.zr_reduce_scatter_adam(plan.handle, _i32(group, "group"),
+                                       _i64(bucket, "bucket"), _i32(dst, "dst"), arr, dt,
+                                       ctypes.byref(h),
                                        _buf(master, "master", ZR_FP32, P),
                                        _buf(m, "m", ZR_FP32, P), _buf(v, "v", ZR_FP32, P),
                                        _buf(param_bf16, "param_bf16", ZR_BF16, P),
@@ -414,14 +443,16 @@ def zr_reduce_scatter_adam_capped(plan, group, bucket, dst, reps, master, m, v,
     arr, dt = _replicas(reps)
     h = _adam(lr, beta1, beta2, eps, step)
     P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
-    _check(_lib.zr_reduce_scatter_adam_capped(plan.handle, int(group), int(bucket),
-                                              int(dst), arr, dt, ctypes.byref(h),
+    _check(_lib.zr_reduce_scatter_adam_capped(plan.handle, _i32(group, "group"),
+                                              _i64(bucket, "bucket"), _i32(dst, "dst"),
+                                              arr, dt, ctypes.byref(h),
                                               _buf(master, "master", ZR_FP32, P),
                                               _buf(m, "m", ZR_FP32, P),
                                               _buf(v, "v", ZR_FP32, P),
                                               _buf(param_bf16, "param_bf16", ZR_BF16, P),
                                               _buf(grad_out, "grad_out", ZR_FP32, P),
-                                              int(max_workgroups), _stream(stream)))
+                                              _i32(max_workgroups, "max_workgroups"),
+                                              _stream(stream)))
 
 
 def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
@@ -429,7 +460,7 @@ def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
     need = max(int(chunk_numel), 0) * n
     arr = (c_vp * max(n, 1))(*[_buf(t, f"rank_bufs[{i}]", ZR_FP32, need).value
                                if t is not None else None for i, t in enumerate(rank_bufs)])
-    _check(_lib.zr_ring_rs_step(arr, n, int(chunk_numel), int(step),
+    _check(_lib.zr_ring_rs_step(arr, n, _i64(chunk_numel, "chunk_numel"), _i32(step, "step"),
                                 _stream(stream)))
 
 
@@ -438,7 +469,8 @@ def zr_ring_ag_step(rank_bufs, chunk_numel, step, stream=None):
     need = max(int(chunk_numel), 0) * n
     arr = (c_vp * max(n, 1))(*[_buf(t, f"rank_bufs[{i}]", ZR_FP32, need).value
                                if t is not None else None for i, t in enumerate(rank_bufs)])
-    _check(_lib.zr_ring_ag_step(arr, n, int(chunk_numel), int(step), _stream(stream)))
+    _check(_lib.zr_ring_ag_step(arr, n, _i64(chunk_numel, "chunk_numel"), _i32(step, "step"),
+                                _stream(stream)))
 
 
 def zr_all_gather_params(plan, group, parts, out, out_base=0, out_len=None,
@@ -450,7 +482,7 @@ def zr_all_gather_params(plan, group, parts, out, out_base=0, out_len=None,
     P = _part_numel(plan, group)
     arr = (c_vp * max(n, 1))(*[(_buf(t, f"parts[{i}]", dt, P).value if t is not None else 0)
                                for i, t in enumerate(parts)])
-    ol = out.numel() if out_len is None else int(out_len)
-    _check(_lib.zr_all_gather_params(plan.handle, int(group), arr, dt,
-                                     _buf(out, "out", dt, ol), int(out_base), ol,
+    ol = out.numel() if out_len is None else _i64(out_len, "out_len")
+    _check(_lib.zr_all_gather_params(plan.handle, _i32(group, "group"), arr, dt,
+                                     _buf(out, "out", dt, ol), _i64(out_base, "out_base"), ol,
                                      _stream(stream)))
