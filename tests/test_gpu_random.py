@@ -1,7 +1,8 @@
 """Randomized parity: random plans (1-2 groups, R up to 17, sp dividing R,
 bucket sizes from 1 element to unbounded, align up to 64), random element
 offsets of every stream, bf16 or fp32 replicas; the fused and unfused calls
-on several ranks, the per-bucket calls composed, and IPG over a random
+on several ranks (and the grid-capped fused call, bit for bit against the
+uncapped one), the per-bucket calls composed, and IPG over a random
 window, each against the oracle (bit-exact; Adam within rel 1e-6 / abs
 1e-7; bf16 param = RNE of the GPU's own master)."""
 
@@ -81,6 +82,19 @@ def _random_case(seed):
             assert_within(host_f32(dm), w_m, what=f"seed {seed} m")
             assert_within(host_f32(dv), w_v, atol=0.0, what=f"seed {seed} v")
             assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"seed {seed} bf16"
+            # the grid-capped call gives the same bits (its own generator, so
+            # the cases drawn above do not depend on it)
+            cap = random.Random(seed * 7919 + k).choice([1, 2, 5, 64, 300])
+            cth, cm, cv = to_dev(th, so), to_dev(m, so), to_dev(v, so)
+            cpb = torch.zeros(P + po + 8, dtype=torch.bfloat16, device="cuda")[po:po + P]
+            cgo = empty_f32(P, go)
+            zr.zr_reduce_scatter_adam_capped(plan, g, -1, k, dreps, cth, cm, cv, cpb, cgo,
+                                             max_workgroups=cap, step=2, **HP)
+            for a_, b_, nm in ((cgo, gout, "grad"), (cth, dth, "master"), (cm, dm, "m"),
+                               (cv, dv, "v")):
+                assert np.array_equal(host_f32(a_).view(np.uint32), host_f32(b_).view(np.uint32)), \
+                    f"seed {seed} g{g} k{k} capped ({cap}) {nm}"
+            assert np.array_equal(host_u16(cpb), host_u16(pb)), f"seed {seed} capped bf16"
             # per-bucket calls compose to the whole
             ob = empty_f32(P, 0)
             for b in range(ref.num_buckets):
