@@ -762,10 +762,27 @@ def setup_copy(torch, zr, workloads):
 
 # ------------------------------------------------------------ CPU baseline
 
+CPU_MIN_SECONDS = 10.0   # single-thread work per CPU baseline (whole passes)
+CPU_MAX_PASSES = 8
+
+
+def _timed_passes(fn):
+    """Runs fn() until at least CPU_MIN_SECONDS have been spent (whole
+    passes, at most CPU_MAX_PASSES); returns (seconds, passes)."""
+    total, passes = 0.0, 0
+    while passes < CPU_MAX_PASSES and (passes == 0 or total < CPU_MIN_SECONDS):
+        t0 = time.perf_counter()
+        fn()
+        total += time.perf_counter() - t0
+        passes += 1
+    return total, passes
+
+
 def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
     """Time the CPU oracle (plan-driven reduce-scatter, Adam, bf16 writeback)
     on every rank's partition of the step (the whole step of all R ranks),
-    inputs already on the host (copies untimed).  Two runs of the same
+    inputs already on the host (copies untimed), in whole passes until at
+    least CPU_MIN_SECONDS of single-thread work.  Two runs of the same
     oracle code: one thread, ranks one after another; then one thread per
     rank (up to the host cores available), all ranks at once -- numpy's
     elementwise loops release the interpreter lock, so the threads run on
@@ -790,26 +807,29 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
         th1, _, _ = adam_oracle(g, masters[k], z, z, step=1, **HP)
         bf16_rne_oracle(th1)
 
-    total = 0.0
-    for k in range(R):
-        t0 = time.perf_counter()
-        one_rank(k)
-        total += time.perf_counter() - t0
+    def whole_step():
+        for k in range(R):
+            one_rank(k)
+
+    total, passes = _timed_passes(whole_step)
     avail = len(os.sched_getaffinity(0))
     threads = max(1, min(R, avail))
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(lambda k: None, range(threads)))          # start the threads
         t0 = time.perf_counter()
-        list(ex.map(one_rank, range(R)))
+        for _ in range(passes):
+            list(ex.map(one_rank, range(R)))
         par = time.perf_counter() - t0
-    byts = (R * 2 + 26) * P * R
+    byts = (R * 2 + 26) * P * R * passes
+    elems = P * R * passes
     return {"value": round(byts / total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "elements_per_s": round(P * R / total), "seconds": round(total, 3),
-            "sample": f"all {R} ranks' partitions of the step: {R} x {P} elements x {R} bf16 "
-                      "replicas (reduce-scatter + Adam + bf16 writeback), numpy single thread",
+            "elements_per_s": round(elems / total), "seconds": round(total, 3),
+            "sample": f"{passes} passes over all {R} ranks' partitions of the step: {R} x {P} "
+                      f"elements x {R} bf16 replicas (reduce-scatter + Adam + bf16 writeback), "
+                      "numpy single thread",
             "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
-                         "elements_per_s": round(P * R / par), "seconds": round(par, 3),
-                         "sample": f"the same {R} partitions, one thread per rank"},
+                         "elements_per_s": round(elems / par), "seconds": round(par, 3),
+                         "sample": f"the same {passes} passes, one thread per rank"},
             "host_cores_available": avail}
 
 
@@ -817,8 +837,9 @@ def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
     """Time the CPU oracle on a fixed chunk of one rank's share: the first
     ``chunk`` partition elements lie inside one slice, so the oracle's
     per-slice steps apply directly (rank-order pre-divided sum of the R fp32
-    replica values, Adam, bf16 writeback); inputs already on the host.  One
-    thread, then one thread per eighth of the chunk."""
+    replica values, Adam, bf16 writeback); inputs already on the host; whole
+    passes until at least CPU_MIN_SECONDS.  One thread, then one thread per
+    eighth of the chunk."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     from oracle.adam import adam_oracle
@@ -835,25 +856,26 @@ def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
         th1, _, _ = adam_oracle(g, th[a:b], z[a:b], z[a:b], step=1, **HP)
         bf16_rne_oracle(th1)
 
-    t0 = time.perf_counter()
-    part(0, n)
-    one = time.perf_counter() - t0
+    one, passes = _timed_passes(lambda: part(0, n))
     avail = len(os.sched_getaffinity(0))
     threads = max(1, min(8, avail))
     cuts = [n * i // threads for i in range(threads + 1)]
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(lambda i: None, range(threads)))
         t0 = time.perf_counter()
-        list(ex.map(lambda i: part(cuts[i], cuts[i + 1]), range(threads)))
+        for _ in range(passes):
+            list(ex.map(lambda i: part(cuts[i], cuts[i + 1]), range(threads)))
         par = time.perf_counter() - t0
-    byts = (R * 4 + 26) * n
+    byts = (R * 4 + 26) * n * passes
     return {"value": round(byts / one / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "elements_per_s": round(n / one), "seconds": round(one, 3),
-            "sample": f"the first {n} elements of rank 0's partition ({R} fp32 replicas, "
-                      f"divisor {D:g}; reduce + Adam + bf16 writeback), numpy single thread",
+            "elements_per_s": round(n * passes / one), "seconds": round(one, 3),
+            "sample": f"{passes} passes over the first {n} elements of rank 0's partition "
+                      f"({R} fp32 replicas, divisor {D:g}; reduce + Adam + bf16 writeback), "
+                      "numpy single thread",
             "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
-                         "elements_per_s": round(n / par), "seconds": round(par, 3),
-                         "sample": f"the same chunk in {threads} pieces, one thread each"},
+                         "elements_per_s": round(n * passes / par), "seconds": round(par, 3),
+                         "sample": f"the same {passes} passes, the chunk in {threads} pieces, "
+                                   "one thread each"},
             "host_cores_available": avail}
 
 
