@@ -162,6 +162,24 @@ def test_binding_rejects_integers_ctypes_would_wrap():
     assert zr.zr_plan_num_buckets(zr.zr_plan_buckets([10, 20], [0, 0], [(2, 1)], 1e1)) == 3
 
 
+def test_prepared_call_checks_its_arguments_once():
+    plan = _tiny_plan()
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    with pytest.raises(zr.ZrError, match="max_workgroups"):
+        zr.prepare_reduce_scatter_adam(plan, 0, 0, reps, buf, buf, buf, max_workgroups=-1)
+    with pytest.raises(zr.ZrError, match="group"):
+        zr.prepare_reduce_scatter_adam(plan, 1, 0, reps, buf, buf, buf)
+    with pytest.raises(zr.ZrError, match="touches 2280"):
+        zr.prepare_reduce_scatter_adam(plan, 0, -1, reps, buf, buf, buf)
+    call = zr.prepare_reduce_scatter_adam(plan, 0, 4, reps, buf, buf, buf)
+    # the C library still validates every call (nothing reaches a GPU here)
+    with pytest.raises(zr.ZrError, match="dst"):
+        call(-1, 1, stream=0)
+    with pytest.raises(zr.ZrError, match="step"):
+        zr.prepare_reduce_scatter_adam(plan, 0, 0, reps, buf, buf, buf)(-1, 0, stream=0)
+
+
 def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
     plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
     g = _FakeTensor(0x1000, 10, "bf16")

@@ -455,6 +455,54 @@ def zr_reduce_scatter_adam_capped(plan, group, bucket, dst, reps, master, m, v,
                                               _stream(stream)))
 
 
+class PreparedReduceScatterAdam:
+    """zr_reduce_scatter_adam -- or, with max_workgroups >= 1,
+    zr_reduce_scatter_adam_capped -- with its arguments checked and marshalled
+    once, for loops that call it per bucket.  Each call passes only the
+    bucket, the Adam step and the stream; the C library validates every call
+    as usual.  Holds references to the tensors, so their memory stays valid
+    while it lives.  One object must not be called from several threads at
+    once (the step is written into its argument struct)."""
+
+    def __init__(self, plan, group, dst, reps, master, m, v, param_bf16=None,
+                 grad_out=None, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                 max_workgroups=0):
+        self._keep = (plan, list(reps), master, m, v, param_bf16, grad_out)
+        self._arr, self._dt = _replicas(reps)
+        self._group = _i32(group, "group")
+        self._dst = _i32(dst, "dst")
+        P = _part_numel(plan, group) if self._dst >= 0 else _padded_numel(plan, group)
+        self._bufs = (_buf(master, "master", ZR_FP32, P), _buf(m, "m", ZR_FP32, P),
+                      _buf(v, "v", ZR_FP32, P),
+                      _buf(param_bf16, "param_bf16", ZR_BF16, P),
+                      _buf(grad_out, "grad_out", ZR_FP32, P))
+        self._h = _adam(lr, beta1, beta2, eps, 1)
+        self._cap = _i32(max_workgroups, "max_workgroups")
+        if self._cap < 0:
+            raise ZrError(ZR_ERR_INVALID, "max_workgroups must be >= 0 (0: uncapped)")
+        self._handle = plan.handle
+
+    def __call__(self, bucket=-1, step=1, stream=None):
+        self._h.step = _i64(step, "step")
+        b = _i64(bucket, "bucket")
+        if self._cap:
+            _check(_lib.zr_reduce_scatter_adam_capped(
+                self._handle, self._group, b, self._dst, self._arr, self._dt,
+                ctypes.byref(self._h), *self._bufs, self._cap, _stream(stream)))
+        else:
+            _check(_lib.zr_reduce_scatter_adam(
+                self._handle, self._group, b, self._dst, self._arr, self._dt,
+                ctypes.byref(self._h), *self._bufs, _stream(stream)))
+
+
+def prepare_reduce_scatter_adam(plan, group, dst, reps, master, m, v, param_bf16=None,
+                                grad_out=None, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                                max_workgroups=0):
+    """A PreparedReduceScatterAdam for these arguments."""
+    return PreparedReduceScatterAdam(plan, group, dst, reps, master, m, v, param_bf16,
+                                     grad_out, lr, beta1, beta2, eps, max_workgroups)
+
+
 def zr_ring_rs_step(rank_bufs, chunk_numel, step, stream=None):
     n = len(rank_bufs)
     need = max(int(chunk_numel), 0) * n
