@@ -504,3 +504,44 @@ def test_large_and_odd_replica_counts(R, sp, is_bf16):
     assert_bits_equal(host_f32(g), want[k], "fused grad")
     w_th, w_m, w_v = adam_oracle(want[k], th, z, z, step=1, **HP)
     assert_within(host_f32(dth), w_th, what="master")
+
+
+# Partition size 2 (mod 4) with align 1 puts odd ranks' bf16 replica windows
+# 4 bytes off the state buffers' 16-byte grid, and state offsets of 1-3
+# elements leave the fp32 streams dword- but not 16-byte-aligned: no phase is
+# slot-aligned for every stream, so these segments take the vector path at a
+# dword-aligned phase (or go element by element where bf16 streams sit an odd
+# number of elements apart).  Every rank, several tiles, against the oracle.
+@pytest.mark.parametrize("is_bf16", [True, False])
+@pytest.mark.parametrize("state_off,pb_off", [(0, 0), (1, 2), (2, 1), (3, 3)])
+def test_dword_aligned_phases(is_bf16, state_off, pb_off):
+    numels = [4 * 1024 * 8 + 16]          # T = 32784, P = 4098 = 2 (mod 4)
+    ref = plan_oracle(numels, [0], [(8, 1)], 1 << 30)
+    plan = zr.zr_plan_buckets(numels, [0], [(8, 1)], 1 << 30)
+    info = ref.groups[0]
+    P, R, T = info.part_numel, info.world, info.total
+    assert P % 4 == 2
+    rng = np.random.default_rng(100 + state_off)
+    reps = [_draw(rng, T, is_bf16, sigma=1e-3) for _ in range(R)]
+    dreps = [to_dev(x) for x in reps]
+    want = reduce_scatter_oracle(ref, 0, reps, is_bf16)
+    for k in range(R):
+        th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(P) * 1e-4).astype(np.float32)
+        v = np.abs(rng.standard_normal(P) * 1e-8).astype(np.float32)
+        first = max(0, min(P, T - k * P))
+        th[first:] = m[first:] = v[first:] = 0.0
+        dth, dm, dv = to_dev(th, state_off), to_dev(m, state_off), to_dev(v, state_off)
+        pb = torch.zeros(P + pb_off + 8, dtype=torch.bfloat16, device="cuda")[pb_off:pb_off + P]
+        go = empty_f32(P, state_off)
+        zr.zr_reduce_scatter_adam(plan, 0, -1, k, dreps, dth, dm, dv, pb, go, step=2, **HP)
+        out = empty_f32(P, state_off)
+        zr.zr_reduce_scatter_local(plan, 0, -1, k, dreps, [out])
+        assert_bits_equal(host_f32(go), want[k], f"rank {k} fused grad")
+        assert_bits_equal(host_f32(out), want[k], f"rank {k} reduced grad")
+        w_th, w_m, w_v = adam_oracle(want[k], th, m, v, step=2, **HP)
+        got = host_f32(dth)
+        assert_within(got, w_th, what=f"rank {k} master")
+        assert_within(host_f32(dm), w_m, what=f"rank {k} m")
+        assert_within(host_f32(dv), w_v, atol=0.0, what=f"rank {k} v")
+        assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"rank {k} bf16"
