@@ -124,14 +124,6 @@ constexpr int64_t kRingAgTileElems = int64_t(kRingAgSlots) * kThreads * VE;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// The same vectors with only dword (4-byte) alignment assumed.  A global load
-// or store of two or four dwords needs a dword-aligned address only (the
-// hardware ignores the two low address bits of dword-or-larger accesses), so
-// the reduce kernels can take the vector path whenever every stream is
-// dword-aligned at a common tile phase, not only when all are slot-aligned.
-typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
-typedef unsigned int u32x2d __attribute__((ext_vector_type(2), aligned(4)));
-typedef float f32x4d __attribute__((ext_vector_type(4), aligned(4)));
 
 // ------------------------------------------------------------ device helpers
 
@@ -195,7 +187,7 @@ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
 // slot (four elements).
 template <typename InT> struct In;
 template <> struct In<uint16_t> {
-  using Vec = u32x2d;
+  using Vec = u32x2;
   __device__ static __forceinline__ float widen(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
@@ -207,7 +199,7 @@ template <> struct In<uint16_t> {
   }
 };
 template <> struct In<float> {
-  using Vec = u32x4d;
+  using Vec = u32x4;
   __device__ static __forceinline__ float widen(float v) { return v; }
   __device__ static __forceinline__ void unpack(Vec w, float* x) {
 #pragma unroll
@@ -247,9 +239,8 @@ __device__ __forceinline__ void adam_elem(const AdamConsts& k, float g,
 // bf16 param / reduced-gradient copies of that slot.  Each destination is a
 // per-tile stream base plus the slot's byte offset (o4 for fp32 streams, o2
 // for the bf16 param); a zero base means "not written".
-template <typename V>
 __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
-                                          V th, V mm, V vv,
+                                          f32x4 th, f32x4 mm, f32x4 vv,
                                           uint64_t master, uint64_t m, uint64_t v,
                                           uint64_t pbf16, uint64_t gout,
                                           uint32_t o4, uint32_t o2) {
@@ -261,12 +252,12 @@ __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
     b[e] = vv[e];
     adam_elem(k, g[e], t[e], a[e], b[e]);
   }
-  st_tile<f32x4d>(master, o4, f32x4d{t[0], t[1], t[2], t[3]});
-  st_tile<f32x4d>(m, o4, f32x4d{a[0], a[1], a[2], a[3]});
-  st_tile<f32x4d>(v, o4, f32x4d{b[0], b[1], b[2], b[3]});
-  if (gout) st_tile<f32x4d>(gout, o4, f32x4d{g[0], g[1], g[2], g[3]});
+  st_tile<f32x4>(master, o4, f32x4{t[0], t[1], t[2], t[3]});
+  st_tile<f32x4>(m, o4, f32x4{a[0], a[1], a[2], a[3]});
+  st_tile<f32x4>(v, o4, f32x4{b[0], b[1], b[2], b[3]});
+  if (gout) st_tile<f32x4>(gout, o4, f32x4{g[0], g[1], g[2], g[3]});
   if (pbf16)
-    st_tile<u32x2d>(pbf16, o2, u32x2d{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
+    st_tile<u32x2>(pbf16, o2, u32x2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
                                     bf16_rne(t[2]) | (bf16_rne(t[3]) << 16)});
 }
 
@@ -423,30 +414,25 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     const int64_t spart =
         kFused ? sg.part + static_cast<int64_t>(sg.dst) * a.state_stride : sg.part;
 
-    // Alignment of every stream at segment offset j, in three grades.
-    // mode 0: each stream's VE elements land on one naturally aligned 16- or
-    // 8-byte access.  mode 1: every stream dword-aligned, the fp32 state and
-    // output streams still 16-byte aligned (whole-line stores).  mode 2:
-    // every stream dword-aligned (enough for the vector accesses, see u32x4d).
-    auto aligned_at = [&](int64_t j, int mode) {
-      const uint64_t in_al = mode == 0 ? VE * sizeof(InT) : 4;
-      const uint64_t st_al = mode == 2 ? 4 : 16;
-      const uint64_t pb_al = mode == 0 ? 8 : 4;
+    // Every stream is slot-aligned at segment offset j (VE elements of 4 or
+    // 2 bytes land on one 16- or 8-byte access).
+    auto slot_aligned = [&](int64_t j) {
       bool ok = true;
       if (!sg.pad)
         for (int r = 0; r < rr; ++r)
-          ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT), in_al);
+          ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT),
+                             VE * sizeof(InT));
       const uint64_t p4 = static_cast<uint64_t>(spart + j) * 4;
       if constexpr (kFused) {
-        ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, st_al) &&
-             aligned(reinterpret_cast<uint64_t>(a.m) + p4, st_al) &&
-             aligned(reinterpret_cast<uint64_t>(a.v) + p4, st_al);
+        ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, 16) &&
+             aligned(reinterpret_cast<uint64_t>(a.m) + p4, 16) &&
+             aligned(reinterpret_cast<uint64_t>(a.v) + p4, 16);
         if (a.pbf16)
           ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) +
-                                 static_cast<uint64_t>(spart + j) * 2, pb_al);
-        if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, st_al);
+                                 static_cast<uint64_t>(spart + j) * 2, 8);
+        if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, 16);
       } else {
-        ok = ok && aligned(a.out[sg.dst] + p4, st_al);
+        ok = ok && aligned(a.out[sg.dst] + p4, 16);
       }
       return ok;
     };
@@ -454,24 +440,21 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     // `period` elements, shifted down by `shift` so the first tile begins at
     // or before offset 0.  Preferred: the phase that puts replica 0's tiles
     // on whole 128-byte lines (the replicas are most of the bytes read; a
-    // tile boundary inside a line makes two workgroups fetch that line), when
-    // every stream is slot-aligned there.  Otherwise the first phase below VE
-    // of the best alignment grade any phase reaches; if no phase leaves every
-    // stream dword-aligned (bf16 streams an odd number of elements apart) the
-    // segment goes element by element.
+    // tile boundary inside a line makes two workgroups fetch that line).
+    // Otherwise the first phase below VE at which every stream is
+    // slot-aligned; if there is none the segment goes element by element.
     int64_t ph = -1, period = VE;
     if (!sg.pad) {
       constexpr int64_t kLineElems = kLineBytes / sizeof(InT);
       const uint64_t b0 = (a.in[0] + static_cast<uint64_t>(sg.flat) * sizeof(InT)) % kLineBytes;
       const int64_t cand = static_cast<int64_t>((kLineBytes - b0) % kLineBytes / sizeof(InT));
-      if (cand < sg.numel && aligned_at(cand, 0)) {
+      if (cand < sg.numel && slot_aligned(cand)) {
         ph = cand;
         period = kLineElems;
       }
     }
-    for (int mode = 0; mode < 3 && ph < 0; ++mode)
-      for (int64_t j = 0; j < VE && ph < 0; ++j)
-        if (aligned_at(j, mode)) ph = j;
+    for (int64_t j = 0; j < VE && ph < 0; ++j)
+      if (slot_aligned(j)) ph = j;
     const bool vec = ph >= 0;
     const int64_t shift = vec ? (period - ph) % period : 0;
     const int64_t rel0 = lt * kTileElems - shift;
@@ -498,7 +481,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
 
     // Issue every load of the tile's slots first.
     Vec w[kSlots][kRL];
-    f32x4d s0[kSlots], s1[kSlots], s2[kSlots];
+    f32x4 s0[kSlots], s1[kSlots], s2[kSlots];
     bool full[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
@@ -514,9 +497,9 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
           }
         }
         if constexpr (kFused) {
-          s0[u] = ld_tile<f32x4d>(b_master, slot * 16);
-          s1[u] = ld_tile<f32x4d>(b_m, slot * 16);
-          s2[u] = ld_tile<f32x4d>(b_v, slot * 16);
+          s0[u] = ld_tile<f32x4>(b_master, slot * 16);
+          s1[u] = ld_tile<f32x4>(b_m, slot * 16);
+          s2[u] = ld_tile<f32x4>(b_v, slot * 16);
         }
       }
     }
@@ -536,7 +519,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
           reduce_slot_rt<InT, kDiv>(a, rr, sg.flat + rel, g);
         }
         if constexpr (!kFused) {
-          st_tile<f32x4d>(b_out, slot * 16, f32x4d{g[0], g[1], g[2], g[3]});
+          st_tile<f32x4>(b_out, slot * 16, f32x4{g[0], g[1], g[2], g[3]});
         } else {
           adam_slot(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
                     slot * 16, slot * 8);
