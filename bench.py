@@ -39,17 +39,20 @@ TRAFFIC_SAME_AS = {}
 
 
 def traffic_for(kernel_key):
-    """HBM bytes per launch measured by rocprofv3 counters for this exact
-    kernel source, or None when absent or stale."""
+    """HBM bytes per launch measured by rocprofv3 counters on exactly the
+    kernel that runs now (its fingerprint in the built library), or None when
+    absent or stale."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    from zero_partition_aware_amd.build import device_code_hash
+    from zero_partition_aware_amd.build import kernel_hashes
     entry = t.get(kernel_key)
-    dev = device_code_hash()
-    if not entry or dev is None or entry.get("device_code_sha") != dev:
+    if not entry or not entry.get("kernel_sha"):
+        return None
+    now = kernel_hashes()
+    if any(now.get(name) != h for name, h in entry["kernel_sha"].items()):
         return None
     return entry.get("hbm_bytes_per_launch")
 

@@ -33,48 +33,80 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# The device code's fingerprint: a hash of the gfx950 code object's
-# instructions (.text), kernel descriptors (.rodata) and kernel metadata
-# (.note), written beside the library at build time.  The rest of the ELF
-# (build ids, symbol tables) differs from compile to compile, and host-side
-# edits leave these sections alone, so counter measurements stay tied to the
-# exact kernels they were taken on.
-DEVICE_SHA = os.path.join(HERE, "libzr.device_sha")
-DEVICE_SECTIONS = (".text", ".rodata", ".note")
+# Per-kernel fingerprints of the device code: for every kernel in the gfx950
+# code object, a hash of its instruction bytes (.text) and of its kernel
+# descriptor (.rodata, register and segment sizes), written beside the
+# library at build time as {demangled kernel name: hash}.  The code holds no
+# relocations or PC-relative references, so a kernel's bytes do not depend on
+# where it sits; the descriptor's code-entry offset, which does, is zeroed
+# before hashing.  A counter measurement stays tied to exactly the kernel it
+# was taken on: host-side edits, or changes to other kernels, leave it valid.
+KERNEL_SHA = os.path.join(HERE, "libzr.kernels.json")
+_KD_ENTRY_OFFSET = slice(16, 24)   # kernel_code_entry_byte_offset in a descriptor
 
 
-def _objcopy():
-    for cand in ("/opt/rocm/llvm/bin/llvm-objcopy", shutil.which("llvm-objcopy")):
+def _llvm_tool(name):
+    for cand in (f"/opt/rocm/llvm/bin/{name}", shutil.which(name)):
         if cand and os.path.exists(cand):
             return cand
-    raise RuntimeError("llvm-objcopy not found: the ROCm LLVM tools are required")
+    raise RuntimeError(f"{name} not found: the ROCm LLVM tools are required")
 
 
-def _device_code_hash(hipcc):
+def _kernel_hashes(hipcc):
     import hashlib
+    import json
     import tempfile
     with tempfile.TemporaryDirectory() as tmp:
         obj = os.path.join(tmp, "dev.o")
         _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "--cuda-device-only",
               "--no-gpu-bundle-output", "-c", os.path.join(CSRC, "zr_kernels.hip"),
               "-o", obj])
-        h = hashlib.sha256()
-        for sec in DEVICE_SECTIONS:
-            out = os.path.join(tmp, "sec.bin")
-            _run([_objcopy(), "--dump-section", f"{sec}={out}", obj])
-            with open(out, "rb") as fh:
-                data = fh.read()
-            h.update(sec.encode() + len(data).to_bytes(8, "little") + data)
-        return h.hexdigest()[:16]
+        readelf = _llvm_tool("llvm-readelf")
+        sections = {}
+        for ln in _run([readelf, "-S", "--wide", obj]).splitlines():
+            f = ln.replace("[ ", "[").split()
+            if len(f) > 5 and f[1] in (".text", ".rodata"):
+                sections[f[1]] = (int(f[3], 16), int(f[4], 16))   # address, file offset
+        funcs, descs = {}, {}
+        for ln in _run([readelf, "-s", "--wide", obj]).splitlines():
+            f = ln.split()
+            if len(f) == 8 and f[3] in ("FUNC", "OBJECT"):
+                addr, size, name = int(f[1], 16), int(f[2]), f[7]
+                if f[3] == "FUNC":
+                    funcs[name] = (addr, size)
+                elif name.endswith(".kd"):
+                    descs[name[:-3]] = (addr, size)
+        with open(obj, "rb") as fh:
+            data = fh.read()
+
+        def read(sec, addr, size):
+            base, off = sections[sec]
+            return data[off + addr - base: off + addr - base + size]
+
+        names = sorted(funcs)
+        demangled = _run(["c++filt"] + names).splitlines() if names else []
+        out = {}
+        for name, dname in zip(names, demangled):
+            if name not in descs:
+                continue
+            kd = bytearray(read(".rodata", *descs[name]))
+            kd[_KD_ENTRY_OFFSET] = bytes(_KD_ENTRY_OFFSET.stop - _KD_ENTRY_OFFSET.start)
+            h = hashlib.sha256(read(".text", *funcs[name]) + bytes(kd))
+            out[dname.strip()] = h.hexdigest()[:16]
+        if not out:
+            raise RuntimeError("no kernels found in the device code object")
+        return json.dumps(out, indent=1, sort_keys=True) + "\n"
 
 
-def device_code_hash():
-    """Fingerprint of the built library's device code (None if not built)."""
+def kernel_hashes():
+    """{demangled kernel name: fingerprint} of the built library's kernels
+    (empty if not built)."""
+    import json
     try:
-        with open(DEVICE_SHA) as fh:
-            return fh.read().strip() or None
-    except OSError:
-        return None
+        with open(KERNEL_SHA) as fh:
+            return json.load(fh)
+    except (OSError, ValueError):
+        return {}
 
 
 def _run(cmd):
@@ -106,8 +138,8 @@ def build(verbose=False):
                  "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
                  "-Wl,--no-undefined", "-o", tmp])
     os.replace(tmp, LIB)
-    with open(DEVICE_SHA, "w") as fh:
-        fh.write(_device_code_hash(hipcc) + "\n")
+    with open(KERNEL_SHA, "w") as fh:
+        fh.write(_kernel_hashes(hipcc))
     if verbose:
         print(out)
     return LIB

@@ -18,15 +18,15 @@ import os
 import shlex
 import sys
 
-from .build import device_code_hash
+from .build import kernel_hashes
 
 
 def _avg_kib(path, match):
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if match in r["Kernel_Name"]]
-    if not vals:
+    rows = [r for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+    if not rows:
         raise SystemExit(f"no dispatch of a kernel matching {match!r} in {path}")
-    return sum(vals) / len(vals), len(vals)
+    vals = [float(r["Counter_Value"]) for r in rows]
+    return sum(vals) / len(vals), len(vals), {r["Kernel_Name"] for r in rows}
 
 
 def main():
@@ -44,18 +44,21 @@ def main():
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
 
-    f_kib, nf = _avg_kib(args.fetch, args.match)
-    w_kib, nw = _avg_kib(args.write, args.match)
-    cf_kib, _ = _avg_kib(args.copy_fetch, args.copy_match)
-    cw_kib, _ = _avg_kib(args.copy_write, args.copy_match)
+    f_kib, nf, f_names = _avg_kib(args.fetch, args.match)
+    w_kib, nw, w_names = _avg_kib(args.write, args.match)
+    cf_kib, _, _ = _avg_kib(args.copy_fetch, args.copy_match)
+    cw_kib, _, _ = _avg_kib(args.copy_write, args.copy_match)
     f_scale = args.copy_bytes / (cf_kib * 1024)
     w_scale = args.copy_bytes / (cw_kib * 1024)
     read_b = f_kib * 1024 * f_scale
     write_b = w_kib * 1024 * w_scale
-    dev = device_code_hash()
-    if dev is None:
-        raise SystemExit("libzr is not built: no device code fingerprint to key the entry to")
-    entry = {"device_code_sha": dev,
+    # The entry is keyed to the fingerprints of the kernels it measured.
+    hashes = kernel_hashes()
+    measured = sorted(f_names | w_names)
+    missing = [n for n in measured if n not in hashes]
+    if missing:
+        raise SystemExit(f"no fingerprint in the built library for {missing}")
+    entry = {"kernel_sha": {n: hashes[n] for n in measured},
              "hbm_bytes_per_launch": round(read_b + write_b),
              "read_bytes_per_launch": round(read_b),
              "write_bytes_per_launch": round(write_b),
