@@ -509,8 +509,9 @@ def test_large_and_odd_replica_counts(R, sp, is_bf16):
 # Partition size 2 (mod 4) with align 1 puts odd ranks' bf16 replica windows
 # 4 bytes off the state buffers' 16-byte grid, and state offsets of 1-3
 # elements leave the fp32 streams dword- but not 16-byte-aligned: no phase is
-# slot-aligned for every stream, so these segments go element by element
-# while the aligned ranks take the vector path.  Every rank, several tiles,
+# slot-aligned for every stream, so the host launches the kernel variant that
+# also accepts dword-aligned phases (bf16 streams an odd number of elements
+# apart would still go element by element).  Every rank, several tiles,
 # against the oracle.
 @pytest.mark.parametrize("is_bf16", [True, False])
 @pytest.mark.parametrize("state_off,pb_off", [(0, 0), (1, 2), (2, 1), (3, 3)])

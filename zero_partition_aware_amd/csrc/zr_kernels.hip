@@ -44,6 +44,7 @@
 #include <new>
 #include <set>
 #include <string>
+#include <type_traits>
 #include <tuple>
 #include <type_traits>
 #include <vector>
@@ -124,6 +125,13 @@ constexpr int64_t kRingAgTileElems = int64_t(kRingAgSlots) * kThreads * VE;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// The same vectors with only dword (4-byte) alignment assumed, for the reduce
+// kernels' dword-aligned variant.  A global load or store of two or four
+// dwords needs a dword-aligned address only (the hardware ignores the two low
+// address bits of dword-or-larger accesses).
+typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned int u32x2d __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4d __attribute__((ext_vector_type(4), aligned(4)));
 
 // ------------------------------------------------------------ device helpers
 
@@ -179,7 +187,7 @@ __device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
   st_global<V>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
 }
 
-__device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
+__host__ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
   return (addr & (bytes - 1)) == 0;
 }
 
@@ -188,10 +196,12 @@ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
 template <typename InT> struct In;
 template <> struct In<uint16_t> {
   using Vec = u32x2;
+  using VecD = u32x2d;
   __device__ static __forceinline__ float widen(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
-  __device__ static __forceinline__ void unpack(Vec w, float* x) {
+  template <typename V>
+  __device__ static __forceinline__ void unpack(V w, float* x) {
     x[0] = __uint_as_float(w[0] << 16);
     x[1] = __uint_as_float(w[0] & 0xffff0000u);
     x[2] = __uint_as_float(w[1] << 16);
@@ -200,8 +210,10 @@ template <> struct In<uint16_t> {
 };
 template <> struct In<float> {
   using Vec = u32x4;
+  using VecD = u32x4d;
   __device__ static __forceinline__ float widen(float v) { return v; }
-  __device__ static __forceinline__ void unpack(Vec w, float* x) {
+  template <typename V>
+  __device__ static __forceinline__ void unpack(V w, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
   }
@@ -239,8 +251,9 @@ __device__ __forceinline__ void adam_elem(const AdamConsts& k, float g,
 // bf16 param / reduced-gradient copies of that slot.  Each destination is a
 // per-tile stream base plus the slot's byte offset (o4 for fp32 streams, o2
 // for the bf16 param); a zero base means "not written".
+template <typename F4, typename U2 = u32x2>
 __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
-                                          f32x4 th, f32x4 mm, f32x4 vv,
+                                          F4 th, F4 mm, F4 vv,
                                           uint64_t master, uint64_t m, uint64_t v,
                                           uint64_t pbf16, uint64_t gout,
                                           uint32_t o4, uint32_t o2) {
@@ -252,12 +265,12 @@ __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
     b[e] = vv[e];
     adam_elem(k, g[e], t[e], a[e], b[e]);
   }
-  st_tile<f32x4>(master, o4, f32x4{t[0], t[1], t[2], t[3]});
-  st_tile<f32x4>(m, o4, f32x4{a[0], a[1], a[2], a[3]});
-  st_tile<f32x4>(v, o4, f32x4{b[0], b[1], b[2], b[3]});
-  if (gout) st_tile<f32x4>(gout, o4, f32x4{g[0], g[1], g[2], g[3]});
+  st_tile<F4>(master, o4, F4{t[0], t[1], t[2], t[3]});
+  st_tile<F4>(m, o4, F4{a[0], a[1], a[2], a[3]});
+  st_tile<F4>(v, o4, F4{b[0], b[1], b[2], b[3]});
+  if (gout) st_tile<F4>(gout, o4, F4{g[0], g[1], g[2], g[3]});
   if (pbf16)
-    st_tile<u32x2>(pbf16, o2, u32x2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
+    st_tile<U2>(pbf16, o2, U2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
                                     bf16_rne(t[2]) | (bf16_rne(t[3]) << 16)});
 }
 
@@ -299,10 +312,8 @@ __device__ __forceinline__ float predivide(const RedArgs& a, float x) {
 }
 
 // Rank-ordered pre-divided sum of one slot from its loaded replica vectors.
-template <typename InT, int R, bool kDiv>
-__device__ __forceinline__ void reduce_slot(const RedArgs& a,
-                                            const typename In<InT>::Vec* w,
-                                            float* acc) {
+template <typename InT, int R, bool kDiv, typename V>
+__device__ __forceinline__ void reduce_slot(const RedArgs& a, const V* w, float* acc) {
   float x[4];
   In<InT>::unpack(w[0], x);
 #pragma unroll
@@ -316,10 +327,9 @@ __device__ __forceinline__ void reduce_slot(const RedArgs& a,
 }
 
 // Same for a run-time replica count (loads issued inside the rank loop).
-template <typename InT, bool kDiv>
+template <typename InT, bool kDiv, typename Vec>
 __device__ __forceinline__ void reduce_slot_rt(const RedArgs& a, int rr, int64_t f,
                                                float* acc) {
-  using Vec = typename In<InT>::Vec;
   const uint64_t off = static_cast<uint64_t>(f) * sizeof(InT);
   float x[4];
   In<InT>::unpack(ld_stream<Vec>(reinterpret_cast<const void*>(a.in[0] + off)), x);
@@ -401,9 +411,15 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
 #define ZR_OCCUPANCY
 #endif
 
-template <typename InT, int R, bool kDiv, bool kFused>
+// kDword: also accept tile phases at which every stream is only
+// dword-aligned (vector types with 4-byte alignment).  The host launches that
+// variant only for selections with a segment at which no phase is
+// slot-aligned, so the common instantiations carry none of its code.
+template <typename InT, int R, bool kDiv, bool kFused, bool kDword>
 __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const RedArgs a) {
-  using Vec = typename In<InT>::Vec;
+  using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
+  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
+  using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
 
@@ -455,6 +471,34 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     }
     for (int64_t j = 0; j < VE && ph < 0; ++j)
       if (slot_aligned(j)) ph = j;
+    if constexpr (kDword) {
+      // Every stream dword-aligned at j; with stores16 the fp32 state and
+      // output streams also 16-byte aligned (whole-line stores), preferred.
+      auto dword_aligned = [&](int64_t j, bool stores16) {
+        const uint64_t st_al = stores16 ? 16 : 4;
+        bool ok = true;
+        if (!sg.pad)
+          for (int r = 0; r < rr; ++r)
+            ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT), 4);
+        const uint64_t p4 = static_cast<uint64_t>(spart + j) * 4;
+        if constexpr (kFused) {
+          ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, st_al) &&
+               aligned(reinterpret_cast<uint64_t>(a.m) + p4, st_al) &&
+               aligned(reinterpret_cast<uint64_t>(a.v) + p4, st_al);
+          if (a.pbf16)
+            ok = ok && aligned(reinterpret_cast<uint64_t>(a.pbf16) +
+                                   static_cast<uint64_t>(spart + j) * 2, 4);
+          if (a.gout) ok = ok && aligned(reinterpret_cast<uint64_t>(a.gout) + p4, st_al);
+        } else {
+          ok = ok && aligned(a.out[sg.dst] + p4, st_al);
+        }
+        return ok;
+      };
+      for (int64_t j = 0; j < VE && ph < 0; ++j)
+        if (dword_aligned(j, true)) ph = j;
+      for (int64_t j = 0; j < VE && ph < 0; ++j)
+        if (dword_aligned(j, false)) ph = j;
+    }
     const bool vec = ph >= 0;
     const int64_t shift = vec ? (period - ph) % period : 0;
     const int64_t rel0 = lt * kTileElems - shift;
@@ -481,7 +525,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
 
     // Issue every load of the tile's slots first.
     Vec w[kSlots][kRL];
-    f32x4 s0[kSlots], s1[kSlots], s2[kSlots];
+    F4 s0[kSlots], s1[kSlots], s2[kSlots];
     bool full[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
@@ -497,9 +541,9 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
           }
         }
         if constexpr (kFused) {
-          s0[u] = ld_tile<f32x4>(b_master, slot * 16);
-          s1[u] = ld_tile<f32x4>(b_m, slot * 16);
-          s2[u] = ld_tile<f32x4>(b_v, slot * 16);
+          s0[u] = ld_tile<F4>(b_master, slot * 16);
+          s1[u] = ld_tile<F4>(b_m, slot * 16);
+          s2[u] = ld_tile<F4>(b_v, slot * 16);
         }
       }
     }
@@ -516,12 +560,12 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         } else if constexpr (R > 0) {
           reduce_slot<InT, R, kDiv>(a, w[u], g);
         } else {
-          reduce_slot_rt<InT, kDiv>(a, rr, sg.flat + rel, g);
+          reduce_slot_rt<InT, kDiv, Vec>(a, rr, sg.flat + rel, g);
         }
         if constexpr (!kFused) {
-          st_tile<f32x4>(b_out, slot * 16, f32x4{g[0], g[1], g[2], g[3]});
+          st_tile<F4>(b_out, slot * 16, F4{g[0], g[1], g[2], g[3]});
         } else {
-          adam_slot(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
+          adam_slot<F4, U2>(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
                     slot * 16, slot * 8);
         }
       } else if (rel < sg.numel && rel + VE > 0) {
@@ -1087,8 +1131,15 @@ zr_status adam_consts(const zr_adam* h, AdamConsts* k) {
 }
 
 template <typename InT, bool kFused>
-zr_status launch_reduce_t(const RedArgs& a, int R, bool div, unsigned grid, hipStream_t st) {
-#define ZR_LAUNCH(RR, DD) reduce_kernel<InT, RR, DD, kFused><<<grid, kThreads, 0, st>>>(a)
+zr_status launch_reduce_t(const RedArgs& a, int R, bool div, bool dword, unsigned grid,
+                          hipStream_t st) {
+#define ZR_LAUNCH(RR, DD)                                                   \
+  do {                                                                      \
+    if (dword)                                                              \
+      reduce_kernel<InT, RR, DD, kFused, true><<<grid, kThreads, 0, st>>>(a); \
+    else                                                                    \
+      reduce_kernel<InT, RR, DD, kFused, false><<<grid, kThreads, 0, st>>>(a); \
+  } while (0)
   if (div) {
     switch (R) {
       case 2: ZR_LAUNCH(2, true); break;
@@ -1194,16 +1245,43 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   a.divisor = static_cast<float>(gi.divisor);
   a.inv_divisor = 1.0f / static_cast<float>(gi.divisor);
   const bool div = !pow2(gi.divisor);
+  // Does some segment have no tile phase at which every stream is
+  // slot-aligned (the kernel's first two choices)?  Then launch the variant
+  // that also accepts dword-aligned phases.
+  auto slot_phase_exists = [&](const Seg& g) {
+    const int64_t spart = fused ? g.part + static_cast<int64_t>(g.dst) * a.state_stride : g.part;
+    for (int64_t j = 0; j < VE; ++j) {
+      bool ok = true;
+      if (!g.pad)
+        for (int r = 0; r < gi.world && ok; ++r)
+          ok = aligned(a.in[r] + static_cast<uint64_t>(g.flat + j) * s, VE * s);
+      const uint64_t p4 = static_cast<uint64_t>(spart + j) * 4;
+      if (fused) {
+        ok = ok && aligned(reinterpret_cast<uint64_t>(a.master) + p4, 16) &&
+             aligned(reinterpret_cast<uint64_t>(a.m) + p4, 16) &&
+             aligned(reinterpret_cast<uint64_t>(a.v) + p4, 16) &&
+             (!a.pbf16 || aligned(reinterpret_cast<uint64_t>(a.pbf16) +
+                                      static_cast<uint64_t>(spart + j) * 2, 8)) &&
+             (!a.gout || aligned(reinterpret_cast<uint64_t>(a.gout) + p4, 16));
+      } else {
+        ok = ok && aligned(a.out[g.dst] + p4, 16);
+      }
+      if (ok) return true;
+    }
+    return false;
+  };
+  bool dword = false;
+  for (int i = 0; i < nseg && !dword; ++i) dword = !slot_phase_exists((*hs)[i]);
   // A capped grid walks the tiles in steps of its size (the kernel's
   // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
   const unsigned grid = max_wgs > 0
       ? static_cast<unsigned>(std::min<int64_t>(grid_for(a.total_tiles, cus), max_wgs))
       : grid_for(a.total_tiles, cus);
   if (dt == ZR_BF16)
-    return fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, grid, stream)
-                 : launch_reduce_t<uint16_t, false>(a, gi.world, div, grid, stream);
-  return fused ? launch_reduce_t<float, true>(a, gi.world, div, grid, stream)
-               : launch_reduce_t<float, false>(a, gi.world, div, grid, stream);
+    return fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, dword, grid, stream)
+                 : launch_reduce_t<uint16_t, false>(a, gi.world, div, dword, grid, stream);
+  return fused ? launch_reduce_t<float, true>(a, gi.world, div, dword, grid, stream)
+               : launch_reduce_t<float, false>(a, gi.world, div, dword, grid, stream);
 }
 
 }  // namespace
