@@ -510,18 +510,21 @@ def test_large_and_odd_replica_counts(R, sp, is_bf16):
 # 4 bytes off the state buffers' 16-byte grid, and state offsets of 1-3
 # elements leave the fp32 streams dword- but not 16-byte-aligned: no phase is
 # slot-aligned for every stream, so the host launches the kernel variant that
-# also accepts dword-aligned phases (bf16 streams an odd number of elements
-# apart would still go element by element).  Every rank, several tiles,
-# against the oracle.
+# also accepts dword-aligned phases, and reads bf16 replicas an odd number of
+# elements off with shifted loads.  Every rank, several tiles, against the
+# oracle.
 @pytest.mark.parametrize("is_bf16", [True, False])
 @pytest.mark.parametrize("state_off,pb_off", [(0, 0), (1, 2), (2, 1), (3, 3)])
-def test_dword_aligned_phases(is_bf16, state_off, pb_off):
-    numels = [4 * 1024 * 8 + 16]          # T = 32784, P = 4098 = 2 (mod 4)
+@pytest.mark.parametrize("p_mod", [2, 1, 3])
+def test_dword_aligned_phases(is_bf16, state_off, pb_off, p_mod):
+    # P = 4096 + p_mod: with P odd, odd ranks' bf16 windows also sit an odd
+    # number of elements off, which the variant reads with shifted loads.
+    numels = [8 * (4096 + p_mod)]
     ref = plan_oracle(numels, [0], [(8, 1)], 1 << 30)
     plan = zr.zr_plan_buckets(numels, [0], [(8, 1)], 1 << 30)
     info = ref.groups[0]
     P, R, T = info.part_numel, info.world, info.total
-    assert P % 4 == 2
+    assert P % 4 == p_mod
     rng = np.random.default_rng(100 + state_off)
     reps = [_draw(rng, T, is_bf16, sigma=1e-3) for _ in range(R)]
     dreps = [to_dev(x) for x in reps]

@@ -187,6 +187,17 @@ __device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
   st_global<V>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
 }
 
+// Four bf16 values that start 2 bytes into a dword (an odd element offset):
+// read the dwords that hold them (bytes -2 .. +10 of the slot, so one value
+// either side) and shift each pair down by 16 bits.  The caller keeps those
+// two extra values inside the segment.
+__device__ __forceinline__ u32x2d ld_bf16_odd(uint64_t base, uint32_t off) {
+  const u32x2d lo = ld_tile<u32x2d>(base - 2, off);
+  const uint32_t hi = ld_tile<uint32_t>(base - 2, off + 8);
+  return u32x2d{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
+                __builtin_amdgcn_alignbit(hi, lo[1], 16)};
+}
+
 __host__ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
   return (addr & (bytes - 1)) == 0;
 }
@@ -420,6 +431,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
   using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
+  constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t> && R > 0;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
 
@@ -460,6 +472,8 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     // Otherwise the first phase below VE at which every stream is
     // slot-aligned; if there is none the segment goes element by element.
     int64_t ph = -1, period = VE;
+    // kOddBf16 variant only: replicas read with ld_bf16_odd (bit r = replica r).
+    uint32_t odd_mask = 0;
     if (!sg.pad) {
       constexpr int64_t kLineElems = kLineBytes / sizeof(InT);
       const uint64_t b0 = (a.in[0] + static_cast<uint64_t>(sg.flat) * sizeof(InT)) % kLineBytes;
@@ -474,10 +488,10 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     if constexpr (kDword) {
       // Every stream dword-aligned at j; with stores16 the fp32 state and
       // output streams also 16-byte aligned (whole-line stores), preferred.
-      auto dword_aligned = [&](int64_t j, bool stores16) {
+      auto dword_aligned = [&](int64_t j, bool stores16, bool reps = true) {
         const uint64_t st_al = stores16 ? 16 : 4;
         bool ok = true;
-        if (!sg.pad)
+        if (!sg.pad && reps)
           for (int r = 0; r < rr; ++r)
             ok = ok && aligned(a.in[r] + static_cast<uint64_t>(sg.flat + j) * sizeof(InT), 4);
         const uint64_t p4 = static_cast<uint64_t>(spart + j) * 4;
@@ -494,10 +508,24 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         }
         return ok;
       };
+      // Preference: whole-line (16-byte-aligned) fp32 stores first, then
+      // plain replica reads.  bf16 replicas an odd number of elements off
+      // the other streams are read with ld_bf16_odd (kOddBf16 variants).
       for (int64_t j = 0; j < VE && ph < 0; ++j)
         if (dword_aligned(j, true)) ph = j;
+      if constexpr (kOddBf16)
+        for (int64_t j = 0; j < VE && ph < 0; ++j)
+          if (dword_aligned(j, true, false)) ph = j;
       for (int64_t j = 0; j < VE && ph < 0; ++j)
         if (dword_aligned(j, false)) ph = j;
+      if constexpr (kOddBf16) {
+        for (int64_t j = 0; j < VE && ph < 0; ++j)
+          if (dword_aligned(j, false, false)) ph = j;
+        if (ph >= 0 && !sg.pad)
+          for (int r = 0; r < R; ++r)
+            if ((a.in[r] + static_cast<uint64_t>(sg.flat + ph) * sizeof(InT)) & 2)
+              odd_mask |= 1u << r;
+      }
     }
     const bool vec = ph >= 0;
     const int64_t shift = vec ? (period - ph) % period : 0;
@@ -531,13 +559,27 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     for (int u = 0; u < kSlots; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
       const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
-      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if constexpr (kOddBf16) {
+        // ld_bf16_odd reads one value either side of the slot.
+        const int64_t lo = odd_mask ? 1 : 0;
+        full[u] = vec && rel >= lo && rel + VE + lo <= sg.numel;
+      } else {
+        full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      }
       if (full[u]) {
         if constexpr (R > 0) {
           if (!sg.pad) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-              w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+            for (int r = 0; r < R; ++r) {
+              if constexpr (kOddBf16) {
+                if ((odd_mask >> r) & 1u)
+                  w[u][r] = ld_bf16_odd(a.in[r] + in_off, slot * VE * sizeof(InT));
+                else
+                  w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+              } else {
+                w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+              }
+            }
           }
         }
         if constexpr (kFused) {
