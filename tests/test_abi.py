@@ -271,3 +271,19 @@ def test_plain_c_client_sees_documented_errors(tmp_path):
     proc = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert proc.returncode == 0, proc.stdout
     assert proc.stdout.strip().endswith("all ok")
+
+
+def test_kernel_fingerprints_cover_the_measured_kernels():
+    """The build writes one fingerprint per kernel of the code object, keyed
+    by the demangled name rocprofv3 reports; every kernel a counter entry in
+    profiles/traffic.json was measured on is still there under that name (a
+    rename would silently turn the bench's traffic figure to null)."""
+    import json
+    from zero_partition_aware_amd.build import kernel_hashes
+    hashes = kernel_hashes()
+    assert len(hashes) >= 50
+    assert all(len(h) == 16 for h in hashes.values())
+    traffic = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for key, entry in traffic.items():
+        for name in entry["kernel_sha"]:
+            assert name in hashes, f"{key}: kernel {name!r} is not in the built library"
