@@ -709,9 +709,13 @@ struct IpgArgs {
   int32_t nseg;
 };
 
-template <typename InT>
+// kDword: when no phase leaves both streams slot-aligned, take the phase
+// that puts main_grad on 16 bytes (there always is one) and read the
+// gradient dword-aligned -- or, for bf16 an odd number of elements off, with
+// ld_bf16_odd.  The host launches that variant only for calls that need it.
+template <typename InT, bool kDword>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
-  using Vec = typename In<InT>::Vec;
+  using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
     const IpgSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
@@ -721,6 +725,13 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
       if (aligned(sg.src + j * sizeof(InT), VE * sizeof(InT)) &&
           aligned(mg + static_cast<uint64_t>(sg.dst + j) * 4, 16))
         j0 = j;
+    bool odd = false;  // kDword only: bf16 gradient read with ld_bf16_odd
+    if constexpr (kDword) {
+      for (int j = 0; j < VE && j0 < 0; ++j)
+        if (aligned(mg + static_cast<uint64_t>(sg.dst + j) * 4, 16)) j0 = j;
+      if constexpr (std::is_same_v<InT, uint16_t>)
+        odd = j0 >= 0 && ((sg.src + static_cast<uint64_t>(j0) * sizeof(InT)) & 2);
+    }
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kIpgTileElems;
     Vec x[kIpgSlots];
@@ -729,9 +740,22 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
 #pragma unroll
     for (int u = 0; u < kIpgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
-      full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      if constexpr (kDword) {
+        // ld_bf16_odd reads one value either side of the slot.
+        const int64_t lo = odd ? 1 : 0;
+        full[u] = vec && rel >= lo && rel + VE + lo <= sg.numel;
+      } else {
+        full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
+      }
       if (full[u]) {
-        x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+        if constexpr (kDword && std::is_same_v<InT, uint16_t>) {
+          if (odd)
+            x[u] = ld_bf16_odd(sg.src + rel * sizeof(InT), 0);
+          else
+            x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+        } else {
+          x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+        }
         cur[u] = ld_stream<f32x4>(a.main_grad + sg.dst + rel);
       }
     }
@@ -1465,8 +1489,24 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
       a.total_tiles = tiles;
       a.main_grad = main_grad;
       const unsigned grid = grid_for(tiles, cus);
-      if (grad_dtype == ZR_BF16) ipg_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(a);
-      else ipg_kernel<float><<<grid, kThreads, 0, stream>>>(a);
+      // The dword-aligned variant is needed when some segment has no phase
+      // at which the gradient and main_grad are both slot-aligned.
+      bool dword = false;
+      const uint64_t mgp = reinterpret_cast<uint64_t>(main_grad);
+      for (int i = 0; i < a.nseg && !dword; ++i) {
+        bool any = false;
+        for (int64_t j = 0; j < VE && !any; ++j)
+          any = aligned(a.seg[i].src + static_cast<uint64_t>(j) * s, VE * s) &&
+                aligned(mgp + static_cast<uint64_t>(a.seg[i].dst + j) * 4, 16);
+        dword = !any;
+      }
+      if (grad_dtype == ZR_BF16) {
+        if (dword) ipg_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
+        else ipg_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+      } else {
+        if (dword) ipg_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
+        else ipg_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+      }
       st = check_launch("ipg_accumulate launch");
       if (st != ZR_OK) return st;
     }
