@@ -155,6 +155,34 @@ def test_adam_partition(n, off, step):
           f"m {max_ulp(gm, w_m)}, v {max_ulp(gv, w_v)}")
 
 
+# fp32 buffers 1-3 elements off a 16-byte boundary with the bf16 output on an
+# even element (or absent): the dword-aligned variant of the Adam kernel.
+# Equal to the oracle, and bit for bit to the same call on aligned copies.
+@pytest.mark.parametrize("offs", [(1, 2), (2, 0), (3, None), (1, 1)])
+def test_adam_partition_dword_offsets(offs):
+    off, pb_off = offs
+    n = 4096 * 5 + 13
+    rng = np.random.default_rng(off)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-7).astype(np.float32)
+    res = {}
+    for how, o, po in (("offset", off, pb_off), ("aligned", 0, 0)):
+        dg, dth, dm, dv = to_dev(g, o), to_dev(th, o), to_dev(m, o), to_dev(v, o)
+        pb = (None if po is None else
+              torch.zeros(n + po + 8, dtype=torch.bfloat16, device="cuda")[po: po + n])
+        zr.zr_adam_partition(dg, dth, dm, dv, pb, step=3, **HP)
+        res[how] = [host_f32(dth), host_f32(dm), host_f32(dv)] + (
+            [] if pb is None else [host_u16(pb)])
+    for a_, b_, nm in zip(res["offset"], res["aligned"], ("master", "m", "v", "bf16")):
+        assert np.array_equal(a_.view(np.uint8), b_.view(np.uint8)), f"{nm}: offset vs aligned"
+    w_th, w_m, w_v = adam_oracle(g, th, m, v, step=3, **HP)
+    assert_within(res["offset"][0], w_th, what="master")
+    assert_within(res["offset"][1], w_m, what="m")
+    assert_within(res["offset"][2], w_v, atol=0.0, what="v")
+
+
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("is_bf16", [False, True])
 def test_fused_equals_unfused_and_oracle(seed, is_bf16):

@@ -645,9 +645,13 @@ struct AdamArgs {
   AdamConsts ac;
 };
 
-// Contiguous partition; kVec: every pointer 16-byte aligned (bf16 8-byte).
-template <bool kVec>
+// Contiguous partition; kVec: every pointer 16-byte aligned (bf16 8-byte),
+// or with kDword only dword-aligned (vector types with 4-byte alignment; the
+// host launches that variant when the pointers are not all slot-aligned).
+template <bool kVec, bool kDword>
 __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
+  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
+  using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
   const int64_t ntiles = (a.n + kAdamTileElems - 1) / kAdamTileElems;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const uint64_t t4 = static_cast<uint64_t>(t) * kAdamTileElems * 4;
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
     const uint64_t b_m = reinterpret_cast<uint64_t>(a.m) + t4;
     const uint64_t b_v = reinterpret_cast<uint64_t>(a.v) + t4;
     const uint64_t b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + t4 / 2 : 0;
-    f32x4 g[kAdamSlots], th[kAdamSlots], mm[kAdamSlots], vv[kAdamSlots];
+    F4 g[kAdamSlots], th[kAdamSlots], mm[kAdamSlots], vv[kAdamSlots];
     bool full[kAdamSlots];
 #pragma unroll
     for (int u = 0; u < kAdamSlots; ++u) {
@@ -664,10 +668,10 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
       const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       full[u] = kVec && j + VE <= a.n;
       if (full[u]) {
-        g[u] = ld_tile<f32x4>(b_g, slot * 16);
-        th[u] = ld_tile<f32x4>(b_master, slot * 16);
-        mm[u] = ld_tile<f32x4>(b_m, slot * 16);
-        vv[u] = ld_tile<f32x4>(b_v, slot * 16);
+        g[u] = ld_tile<F4>(b_g, slot * 16);
+        th[u] = ld_tile<F4>(b_master, slot * 16);
+        mm[u] = ld_tile<F4>(b_m, slot * 16);
+        vv[u] = ld_tile<F4>(b_v, slot * 16);
       }
     }
 #pragma unroll
@@ -676,8 +680,8 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
       const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       if (full[u]) {
         const float gg[4] = {g[u][0], g[u][1], g[u][2], g[u][3]};
-        adam_slot(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
-                  slot * 16, slot * 8);
+        adam_slot<F4, U2>(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
+                          slot * 16, slot * 8);
       } else if (j < a.n) {
         const int64_t e1 = j + VE < a.n ? j + VE : a.n;
         for (int64_t e = j; e < e1; ++e) {
@@ -1425,9 +1429,13 @@ extern "C" zr_status zr_adam_partition(const zr_adam* h, const float* grad, floa
   const bool vec = elem_aligned(grad, 16) && elem_aligned(master, 16) &&
                    elem_aligned(m, 16) && elem_aligned(v, 16) &&
                    (!param_bf16 || elem_aligned(param_bf16, 8));
+  // fp32 pointers are always dword-aligned; the bf16 output must be too
+  // for its 8-byte stores (an even element offset).
+  const bool dword = !param_bf16 || elem_aligned(param_bf16, 4);
   const unsigned grid = grid_for((n + kAdamTileElems - 1) / kAdamTileElems, cus);
-  if (vec) adam_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-  else adam_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+  if (vec) adam_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+  else if (dword) adam_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
+  else adam_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
   return check_launch("adam_partition launch");
 }
 
