@@ -794,7 +794,12 @@ struct CopyArgs {
   int32_t nseg;
 };
 
+// kDword: when no phase leaves source and destination both 16-byte aligned,
+// take the destination's (whole-line stores) and read the source merely
+// dword-aligned; the host launches that variant only for calls that need it.
+template <bool kDword>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
+  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
     const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
@@ -805,21 +810,24 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
       if (aligned(reinterpret_cast<uint64_t>(s + j), 16) &&
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
+    if constexpr (kDword)
+      for (int j = 0; j < VE && j0 < 0; ++j)
+        if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kCopyTileElems;
-    f32x4 x[kCopySlots];
+    F4 x[kCopySlots];
     bool full[kCopySlots];
 #pragma unroll
     for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
-      if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
+      if (full[u]) x[u] = ld_stream<F4>(s + rel);
     }
 #pragma unroll
     for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
-        st_stream<f32x4>(d + rel, x[u]);
+        st_stream<F4>(d + rel, x[u]);
       } else if (rel < sg.numel && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
@@ -910,8 +918,13 @@ __host__ __device__ constexpr int64_t gather_tile_elems() {
   return kGatherTileBytes / static_cast<int64_t>(sizeof(T));
 }
 
-template <typename T>
+// kDword: when no phase leaves a partition and the output both 16-byte
+// aligned, take the output's (whole-line stores) and read the partition
+// merely dword-aligned (bf16 partitions an odd number of elements off still
+// go element by element); the host launches that variant only when needed.
+template <typename T, bool kDword>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
+  using LV = std::conditional_t<kDword, u32x4d, u32x4>;
   constexpr int ES = sizeof(T);
   constexpr int GV = 16 / ES;                          // elements per slot
   constexpr int64_t TE = gather_tile_elems<T>();       // elements per tile
@@ -923,6 +936,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
     int j0 = -1;
     for (int j = 0; j < GV && j0 < 0; ++j)
       if (aligned(sg.src + j * ES, 16) && aligned(sg.dst + j * ES, 16)) j0 = j;
+    if constexpr (kDword)
+      for (int j = 0; j < GV && j0 < 0; ++j)
+        if (aligned(sg.src + j * ES, 4) && aligned(sg.dst + j * ES, 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - GV : 0) + lt * TE;
     const uint64_t bs = sg.src + rel0 * ES, bd = sg.dst + rel0 * ES;
@@ -933,7 +949,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
       const int64_t rel = rel0 + static_cast<int64_t>(slot) * GV;
       full[u] = vec && rel >= 0 && rel + GV <= sg.numel;
-      if (full[u]) x[u] = ld_tile<u32x4>(bs, slot * 16);
+      if (full[u]) x[u] = ld_tile<LV>(bs, slot * 16);
     }
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
@@ -1555,7 +1571,18 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
     a.dst = part_out;
     a.nseg = nseg;
     a.total_tiles = (*hs)[nseg].tile0;
-    copy_kernel<<<grid_for(a.total_tiles, cus), kThreads, 0, stream>>>(a);
+    // The dword-aligned variant is needed when some segment has no phase at
+    // which source and destination are both 16-byte aligned.
+    bool dword = false;
+    for (int i = 0; i < nseg && !dword; ++i) {
+      const uint64_t sa = reinterpret_cast<uint64_t>(bucket_layout_src + (*hs)[i].flat);
+      const uint64_t da = reinterpret_cast<uint64_t>(part_out + (*hs)[i].part);
+      bool any = false;
+      for (uint64_t j = 0; j < VE && !any; ++j) any = aligned(sa + 4 * j, 16) && aligned(da + 4 * j, 16);
+      dword = !any;
+    }
+    if (dword) copy_kernel<true><<<grid_for(a.total_tiles, cus), kThreads, 0, stream>>>(a);
+    else copy_kernel<false><<<grid_for(a.total_tiles, cus), kThreads, 0, stream>>>(a);
     return check_launch("copy_grads_in_partition launch");
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
@@ -1606,8 +1633,23 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
     int device = 0, cus = 1;
     zr_status st = device_info(&device, &cus);
     if (st != ZR_OK) return st;
-    if (dtype == ZR_BF16) gather_kernel<uint16_t><<<grid_for(tiles, cus), kThreads, 0, stream>>>(a);
-    else gather_kernel<float><<<grid_for(tiles, cus), kThreads, 0, stream>>>(a);
+    // The dword-aligned variant is needed when some partition has no phase
+    // at which it and the output are both 16-byte aligned.
+    bool dword = false;
+    for (int i = 0; i < n && !dword; ++i) {
+      bool any = false;
+      for (int64_t j = 0; j < 16 / static_cast<int64_t>(es) && !any; ++j)
+        any = aligned(a.seg[i].src + j * es, 16) && aligned(a.seg[i].dst + j * es, 16);
+      dword = !any;
+    }
+    const unsigned grid = grid_for(tiles, cus);
+    if (dtype == ZR_BF16) {
+      if (dword) gather_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
+      else gather_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+    } else {
+      if (dword) gather_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
+      else gather_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+    }
     return check_launch("all_gather_params launch");
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
