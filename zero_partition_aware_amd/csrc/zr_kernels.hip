@@ -125,10 +125,13 @@ constexpr int64_t kRingAgTileElems = int64_t(kRingAgSlots) * kThreads * VE;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// The same vectors with only dword (4-byte) alignment assumed, for the reduce
-// kernels' dword-aligned variant.  A global load or store of two or four
-// dwords needs a dword-aligned address only (the hardware ignores the two low
-// address bits of dword-or-larger accesses).
+// The same vectors with only dword (4-byte) alignment assumed, for the
+// kernels' dword-aligned variants (reduce, IPG, Adam, copy, all-gather).  A
+// global load or store of two or four dwords needs a dword-aligned address
+// only (the hardware ignores the two low address bits of dword-or-larger
+// accesses).  Each variant is a separate instantiation that the host launches
+// only when some segment has no phase at which every stream is slot-aligned,
+// so the common instantiations carry none of its code.
 typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
 typedef unsigned int u32x2d __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4d __attribute__((ext_vector_type(4), aligned(4)));
