@@ -23,12 +23,16 @@
  * Conventions for every call:
  *   - Device memory is owned by the caller (e.g. torch tensors passed as raw
  *     device pointers).  The library never frees or reallocates it.
- *     Pointers need only be element-aligned.  The vectorised path needs the
+ *     Pointers need only be element-aligned.  The fastest path needs the
  *     streams of a segment to share one 4-element phase (16-byte accesses
- *     for fp32, 8-byte for bf16); elements it cannot cover go one by one.
- *     Replica tiles are placed on whole 128-byte lines whenever the other
- *     streams allow it, so buffers whose starts share their offset within a
- *     line stream fastest.
+ *     for fp32, 8-byte for bf16); otherwise a variant takes the vector path
+ *     with streams merely 4-byte aligned (bf16 streams an odd number of
+ *     elements apart read with shifted loads in the reduce and IPG calls,
+ *     one by one in the all-gather), somewhat slower.  Partition sizes that
+ *     are a multiple of 4 (align >= 4 in zr_plan_buckets) keep every rank on
+ *     the fastest path.  Replica tiles are placed on whole 128-byte lines
+ *     whenever the other streams allow it, so buffers whose starts share
+ *     their offset within a line stream fastest.
  *   - The library owns a plan (create with zr_plan_buckets, free with
  *     zr_plan_free).  A plan is immutable; small device tables derived from
  *     it are built on first use (a synchronous upload) and freed with it.
