@@ -27,8 +27,7 @@
  *     streams of a segment to share one 4-element phase (16-byte accesses
  *     for fp32, 8-byte for bf16); otherwise a variant takes the vector path
  *     with streams merely 4-byte aligned (bf16 streams an odd number of
- *     elements apart read with shifted loads in the reduce and IPG calls,
- *     one by one in the all-gather), somewhat slower.  Partition sizes that
+ *     elements apart read with shifted loads), somewhat slower.  Partition sizes that
  *     are a multiple of 4 (align >= 4 in zr_plan_buckets) keep every rank on
  *     the fastest path.  Replica tiles are placed on whole 128-byte lines
  *     whenever the other streams allow it, so buffers whose starts share

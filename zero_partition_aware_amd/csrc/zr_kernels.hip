@@ -201,6 +201,16 @@ __device__ __forceinline__ u32x2d ld_bf16_odd(uint64_t base, uint32_t off) {
                 __builtin_amdgcn_alignbit(hi, lo[1], 16)};
 }
 
+// The same for a 16-byte slot of eight bf16 values (the all-gather's slot).
+__device__ __forceinline__ u32x4d ld_bf16x8_odd(uint64_t base, uint32_t off) {
+  const u32x4d lo = ld_tile<u32x4d>(base - 2, off);
+  const uint32_t hi = ld_tile<uint32_t>(base - 2, off + 16);
+  return u32x4d{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
+                __builtin_amdgcn_alignbit(lo[2], lo[1], 16),
+                __builtin_amdgcn_alignbit(lo[3], lo[2], 16),
+                __builtin_amdgcn_alignbit(hi, lo[3], 16)};
+}
+
 __host__ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) {
   return (addr & (bytes - 1)) == 0;
 }
@@ -923,8 +933,8 @@ __host__ __device__ constexpr int64_t gather_tile_elems() {
 
 // kDword: when no phase leaves a partition and the output both 16-byte
 // aligned, take the output's (whole-line stores) and read the partition
-// merely dword-aligned (bf16 partitions an odd number of elements off still
-// go element by element); the host launches that variant only when needed.
+// merely dword-aligned, or for bf16 an odd number of elements off with
+// ld_bf16x8_odd; the host launches that variant only when needed.
 template <typename T, bool kDword>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
   using LV = std::conditional_t<kDword, u32x4d, u32x4>;
@@ -939,9 +949,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
     int j0 = -1;
     for (int j = 0; j < GV && j0 < 0; ++j)
       if (aligned(sg.src + j * ES, 16) && aligned(sg.dst + j * ES, 16)) j0 = j;
-    if constexpr (kDword)
+    bool odd = false;  // kDword bf16 only: partition read with ld_bf16x8_odd
+    if constexpr (kDword) {
       for (int j = 0; j < GV && j0 < 0; ++j)
         if (aligned(sg.src + j * ES, 4) && aligned(sg.dst + j * ES, 16)) j0 = j;
+      if constexpr (ES == 2) {
+        for (int j = 0; j < GV && j0 < 0; ++j)
+          if (aligned(sg.dst + j * ES, 16)) j0 = j;
+        odd = j0 >= 0 && ((sg.src + static_cast<uint64_t>(j0) * ES) & 2);
+      }
+    }
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - GV : 0) + lt * TE;
     const uint64_t bs = sg.src + rel0 * ES, bd = sg.dst + rel0 * ES;
@@ -951,8 +968,15 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
     for (int u = 0; u < GS; ++u) {
       const int slot = u * kThreads + static_cast<int>(threadIdx.x);
       const int64_t rel = rel0 + static_cast<int64_t>(slot) * GV;
-      full[u] = vec && rel >= 0 && rel + GV <= sg.numel;
-      if (full[u]) x[u] = ld_tile<LV>(bs, slot * 16);
+      if constexpr (kDword && ES == 2) {
+        // ld_bf16x8_odd reads one value either side of the slot.
+        const int64_t lo = odd ? 1 : 0;
+        full[u] = vec && rel >= lo && rel + GV + lo <= sg.numel;
+        if (full[u]) x[u] = odd ? ld_bf16x8_odd(bs, slot * 16) : ld_tile<LV>(bs, slot * 16);
+      } else {
+        full[u] = vec && rel >= 0 && rel + GV <= sg.numel;
+        if (full[u]) x[u] = ld_tile<LV>(bs, slot * 16);
+      }
     }
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
