@@ -577,3 +577,37 @@ def test_dword_aligned_phases(is_bf16, state_off, pb_off, p_mod):
         assert_within(host_f32(dm), w_m, what=f"rank {k} m")
         assert_within(host_f32(dv), w_v, atol=0.0, what=f"rank {k} v")
         assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"rank {k} bf16"
+
+
+# Replica counts without a compiled specialization (the rank loop runs at run
+# time) with an odd partition size: the bf16 replicas of odd ranks sit an odd
+# number of elements off and are read with shifted loads inside that loop.
+@pytest.mark.parametrize("R", [5, 12])
+def test_dword_phases_runtime_replica_count(R):
+    P = 2 * 4096 + 1
+    numels = [R * P - 3]
+    ref = plan_oracle(numels, [0], [(R, 1)], 1 << 30)
+    plan = zr.zr_plan_buckets(numels, [0], [(R, 1)], 1 << 30)
+    info = ref.groups[0]
+    assert info.part_numel == P and P % 2 == 1
+    T = info.total
+    rng = np.random.default_rng(R)
+    reps = [_draw(rng, T, True, sigma=1e-3) for _ in range(R)]
+    dreps = [to_dev(x) for x in reps]
+    want = reduce_scatter_oracle(ref, 0, reps, True)
+    for k in range(R):
+        th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+        first = max(0, min(P, T - k * P))
+        th[first:] = 0.0
+        z = np.zeros(P, np.float32)
+        dth, dm, dv = to_dev(th), to_dev(z), to_dev(z)
+        pb = torch.zeros(P, dtype=torch.bfloat16, device="cuda")
+        go = empty_f32(P)
+        zr.zr_reduce_scatter_adam(plan, 0, -1, k, dreps, dth, dm, dv, pb, go, **HP)
+        assert_bits_equal(host_f32(go), want[k], f"rank {k} fused grad")
+        w_th, w_m, w_v = adam_oracle(want[k], th, z, z, step=1, **HP)
+        got = host_f32(dth)
+        assert_within(got, w_th, what=f"rank {k} master")
+        assert_within(host_f32(dm), w_m, what=f"rank {k} m")
+        assert_within(host_f32(dv), w_v, atol=0.0, what=f"rank {k} v")
+        assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"rank {k} bf16"

@@ -351,16 +351,23 @@ __device__ __forceinline__ void reduce_slot(const RedArgs& a, const V* w, float*
 }
 
 // Same for a run-time replica count (loads issued inside the rank loop).
-template <typename InT, bool kDiv, typename Vec>
+// kOdd: replicas whose bit is set in odd_mask are read with ld_bf16_odd.
+template <typename InT, bool kDiv, typename Vec, bool kOdd = false>
 __device__ __forceinline__ void reduce_slot_rt(const RedArgs& a, int rr, int64_t f,
-                                               float* acc) {
+                                               float* acc, uint64_t odd_mask = 0) {
   const uint64_t off = static_cast<uint64_t>(f) * sizeof(InT);
+  auto load = [&](int r) -> Vec {
+    if constexpr (kOdd) {
+      if ((odd_mask >> r) & 1u) return ld_bf16_odd(a.in[r] + off, 0);
+    }
+    return ld_stream<Vec>(reinterpret_cast<const void*>(a.in[r] + off));
+  };
   float x[4];
-  In<InT>::unpack(ld_stream<Vec>(reinterpret_cast<const void*>(a.in[0] + off)), x);
+  In<InT>::unpack(load(0), x);
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = (rr == 1) ? x[e] : predivide<kDiv>(a, x[e]);
   for (int r = 1; r < rr; ++r) {
-    In<InT>::unpack(ld_stream<Vec>(reinterpret_cast<const void*>(a.in[r] + off)), x);
+    In<InT>::unpack(load(r), x);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] = acc[e] + predivide<kDiv>(a, x[e]);
   }
@@ -444,7 +451,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
   using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
-  constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t> && R > 0;
+  constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t>;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
 
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
     // slot-aligned; if there is none the segment goes element by element.
     int64_t ph = -1, period = VE;
     // kOddBf16 variant only: replicas read with ld_bf16_odd (bit r = replica r).
-    uint32_t odd_mask = 0;
+    uint64_t odd_mask = 0;
     if (!sg.pad) {
       constexpr int64_t kLineElems = kLineBytes / sizeof(InT);
       const uint64_t b0 = (a.in[0] + static_cast<uint64_t>(sg.flat) * sizeof(InT)) % kLineBytes;
@@ -535,9 +542,9 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         for (int64_t j = 0; j < VE && ph < 0; ++j)
           if (dword_aligned(j, false, false)) ph = j;
         if (ph >= 0 && !sg.pad)
-          for (int r = 0; r < R; ++r)
+          for (int r = 0; r < rr; ++r)
             if ((a.in[r] + static_cast<uint64_t>(sg.flat + ph) * sizeof(InT)) & 2)
-              odd_mask |= 1u << r;
+              odd_mask |= uint64_t(1) << r;
       }
     }
     const bool vec = ph >= 0;
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(const Red
         } else if constexpr (R > 0) {
           reduce_slot<InT, R, kDiv>(a, w[u], g);
         } else {
-          reduce_slot_rt<InT, kDiv, Vec>(a, rr, sg.flat + rel, g);
+          reduce_slot_rt<InT, kDiv, Vec, kOddBf16>(a, rr, sg.flat + rel, g, odd_mask);
         }
         if constexpr (!kFused) {
           st_tile<F4>(b_out, slot * 16, F4{g[0], g[1], g[2], g[3]});
