@@ -83,3 +83,23 @@ def test_ring_all_reduce_integer_equals_sum_everywhere():
     total = sum(b.astype(np.int64) for b in bufs).astype(np.float32)
     for k in range(n):
         assert np.array_equal(host_f32(dev[k]), total)
+
+
+# Rank buffers starting at different offsets within a 16-byte line: no phase
+# aligns a chunk of one rank with the same chunk of the previous one, so the
+# steps take their dword-aligned variants.  RS then AG against the oracle.
+@pytest.mark.parametrize("n,chunk", [(8, 4096 * 2 + 3), (3, 999)])
+def test_ring_steps_with_misaligned_rank_buffers(n, chunk):
+    rng = np.random.default_rng(100 + n)
+    bufs = [rng.standard_normal(n * chunk).astype(np.float32) for _ in range(n)]
+    dev = [to_dev(b, k % 4) for k, b in enumerate(bufs)]
+    for s in range(n - 1):
+        zr.zr_ring_rs_step(dev, chunk, s)
+    rs, _ = ring_reduce_scatter_oracle(bufs)
+    for k in range(n):
+        assert_bits_equal(host_f32(dev[k]), rs[k], f"rank {k} after reduce-scatter")
+    for s in range(n - 1):
+        zr.zr_ring_ag_step(dev, chunk, s)
+    want, _ = ring_all_gather_oracle(rs)
+    for k in range(n):
+        assert_bits_equal(host_f32(dev[k]), want[k], f"rank {k} after all-gather")

@@ -867,7 +867,9 @@ struct RingArgs {
   int32_t step;
 };
 
+template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
+  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   const int64_t total = a.tiles_per_rank * a.n;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
@@ -882,16 +884,20 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
       if (aligned(reinterpret_cast<uint64_t>(s + j), 16) &&
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
+    if constexpr (kDword)   // the destination's phase; the source dword-aligned
+      for (int j = 0; j < VE && j0 < 0; ++j)
+        if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingTileElems;
-    f32x4 x[kRingSlots], y[kRingSlots];
+    F4 x[kRingSlots];
+    f32x4 y[kRingSlots];
     bool full[kRingSlots];
 #pragma unroll
     for (int u = 0; u < kRingSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
       if (full[u]) {
-        x[u] = ld_stream<f32x4>(s + rel);
+        x[u] = ld_stream<F4>(s + rel);
         y[u] = ld_stream<f32x4>(d + rel);
       }
     }
@@ -1003,7 +1009,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
 
 // Ring all-gather step: rank k copies chunk (k - step - 1) mod n from rank
 // k-1's buffer into its own.
+template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
+  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   const int64_t total = a.tiles_per_rank * a.n;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
@@ -1018,15 +1026,18 @@ __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
       if (aligned(reinterpret_cast<uint64_t>(s + j), 16) &&
           aligned(reinterpret_cast<uint64_t>(d + j), 16))
         j0 = j;
+    if constexpr (kDword)   // the destination's phase; the source dword-aligned
+      for (int j = 0; j < VE && j0 < 0; ++j)
+        if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingAgTileElems;
-    f32x4 x[kRingAgSlots];
+    F4 x[kRingAgSlots];
     bool full[kRingAgSlots];
 #pragma unroll
     for (int u = 0; u < kRingAgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
-      if (full[u]) x[u] = ld_stream<f32x4>(s + rel);
+      if (full[u]) x[u] = ld_stream<F4>(s + rel);
     }
 #pragma unroll
     for (int u = 0; u < kRingAgSlots; ++u) {
@@ -1692,6 +1703,21 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
 
 // Shared validation of the ring steps.
 namespace {
+// Does some rank's chunk of this step have no phase at which its source (the
+// previous rank's buffer) and destination are both 16-byte aligned?  The chunk
+// index of rank k is (k - step - lag) mod n (lag 2 for the reduce-scatter
+// steps, 1 for the all-gather steps).
+bool ring_needs_dword(const RingArgs& a, int lag) {
+  for (int k = 0; k < a.n; ++k) {
+    int c = (k - a.step - lag) % a.n;
+    if (c < 0) c += a.n;
+    const int prev = k == 0 ? a.n - 1 : k - 1;
+    const uint64_t off = static_cast<uint64_t>(c) * static_cast<uint64_t>(a.chunk) * 4;
+    if ((a.buf[k] + off - (a.buf[prev] + off)) % 16 != 0) return true;
+  }
+  return false;
+}
+
 zr_status ring_args(float* const* rank_bufs, int32_t n_ranks, int64_t chunk_numel,
                     int32_t step, int64_t tile, RingArgs* a) {
   if (n_ranks < 2 || n_ranks > ZR_MAX_WORLD)
@@ -1730,7 +1756,9 @@ extern "C" zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
   if (st != ZR_OK) return st;
-  ring_ag_kernel<<<grid_for(a.tiles_per_rank * n_ranks, cus), kThreads, 0, stream>>>(a);
+  const unsigned grid = grid_for(a.tiles_per_rank * n_ranks, cus);
+  if (ring_needs_dword(a, 1)) ring_ag_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+  else ring_ag_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   return check_launch("ring_ag_step launch");
 }
 
@@ -1744,6 +1772,8 @@ extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
   if (st != ZR_OK) return st;
-  ring_kernel<<<grid_for(a.tiles_per_rank * n_ranks, cus), kThreads, 0, stream>>>(a);
+  const unsigned grid = grid_for(a.tiles_per_rank * n_ranks, cus);
+  if (ring_needs_dword(a, 2)) ring_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+  else ring_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   return check_launch("ring_rs_step launch");
 }
