@@ -34,12 +34,20 @@
  *     their offset within a line stream fastest.
  *   - The library owns a plan (create with zr_plan_buckets, free with
  *     zr_plan_free).  A plan is immutable; small device tables derived from
- *     it are built on first use (a synchronous upload) and freed with it.
- *     Each (group, bucket, dst, device) selection has its own table, so a
- *     call recorded into a HIP graph must not be that selection's first:
- *     make it once outside the capture (the upload allocates and copies).
+ *     it are built on first use and freed with it.  The first use of a
+ *     (group, bucket, dst, device) selection that needs a table allocates it
+ *     and uploads it synchronously (one hipMalloc and one hipMemcpy of 48
+ *     bytes per segment, typically tens of microseconds); later calls reuse
+ *     it.  Reduce selections of at most two segments whose launches span
+ *     16K-256K tiles carry their segments in the kernel arguments and need
+ *     no table.  A call recorded into a HIP graph must not be the first use
+ *     of a selection that needs a table: make it once outside the capture.
  *   - Work is enqueued on the caller's HIP stream; nothing synchronises
- *     implicitly.  Completion is the caller's stream synchronisation.
+ *     implicitly.  Completion is the caller's stream synchronisation.  One
+ *     call may enqueue several kernel launches: selections whose traffic
+ *     exceeds about 2 GiB are cut into equal launches of at most that much
+ *     (in one long launch the GPU's XCDs drift apart in the address space,
+ *     which costs bandwidth; a launch boundary realigns them).
  *   - Every call returns a zr_status.  Arguments are validated before any
  *     work is enqueued; on failure no output is touched and zr_last_error()
  *     returns a message (thread-local).  No C++ exception crosses the ABI.

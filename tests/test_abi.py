@@ -183,13 +183,51 @@ def test_prepared_call_checks_its_arguments_once():
 def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
     plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
     g = _FakeTensor(0x1000, 10, "bf16")
+    g20 = _FakeTensor(0x2000, 20, "bf16")
     mg = _FakeTensor(0x100000, 40)
     with pytest.raises(zr.ZrError, match="share a group"):
-        zr.zr_ipg_accumulate(plan, [0, 1], [g, g], mg, stream=0)
+        zr.zr_ipg_accumulate(plan, [0, 1], [g, g20], mg, stream=0)
     with pytest.raises(zr.ZrError, match="twice"):
         zr.zr_ipg_accumulate(plan, [0, 0], [g, g], mg, stream=0)
     with pytest.raises(zr.ZrError, match="past"):
         zr.zr_ipg_accumulate(plan, [0], [g], mg, window_base=1, window_len=40, stream=0)
+
+
+def test_ipg_rejects_gradient_smaller_than_its_param():
+    """A gradient tensor must hold its parameter's elements: the kernel would
+    otherwise read past it."""
+    plan = _tiny_plan()
+    mg = _FakeTensor(0x100000, 2280)
+    with pytest.raises(zr.ZrError, match=r"grads\[1\] holds 2111 elements; the call touches 2112"):
+        zr.zr_ipg_accumulate(plan, [0, 1], [_FakeTensor(0x1000, 37, "bf16"),
+                                            _FakeTensor(0x2000, 2111, "bf16")], mg, stream=0)
+    with pytest.raises(zr.ZrError, match="holds 1 elements"):
+        zr.zr_ipg_accumulate(plan, [2], [_FakeTensor(0x1000, 1, "bf16")], mg, stream=0)
+
+
+def test_binding_checks_list_lengths_against_the_group():
+    """The C calls index the replica, output and partition arrays by rank, so a
+    list of the wrong length is refused before the call."""
+    plan = _tiny_plan()                       # one group of 4 replicas
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    whole = _FakeTensor(0x200000, 2280)
+    for short in (reps[:2], reps + reps[:1]):
+        with pytest.raises(zr.ZrError, match="reps has"):
+            zr.zr_reduce_scatter_local(plan, 0, -1, 0, short, [buf], stream=0)
+        with pytest.raises(zr.ZrError, match="reps has"):
+            zr.zr_reduce_scatter_adam(plan, 0, -1, 0, short, buf, buf, buf, stream=0)
+        with pytest.raises(zr.ZrError, match="reps has"):
+            zr.zr_reduce_scatter_adam_capped(plan, 0, -1, 0, short, buf, buf, buf,
+                                             max_workgroups=4, stream=0)
+        with pytest.raises(zr.ZrError, match="reps has"):
+            zr.prepare_reduce_scatter_adam(plan, 0, 0, short, buf, buf, buf)
+    with pytest.raises(zr.ZrError, match="part_out has 3 entries; the call needs 4"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, -1, reps, [buf] * 3, stream=0)
+    with pytest.raises(zr.ZrError, match="part_out has 2 entries; the call needs 1"):
+        zr.zr_reduce_scatter_local(plan, 0, -1, 1, reps, [buf] * 2, stream=0)
+    with pytest.raises(zr.ZrError, match="parts has 3 entries"):
+        zr.zr_all_gather_params(plan, 0, [buf] * 3, whole, stream=0)
 
 
 def test_ring_rejects_bad_step_and_overlap():

@@ -26,6 +26,17 @@
 // instruction the same hint costs half the bandwidth, so the whole-line store
 // layout above is what makes it pay.)
 //
+// Long selections are cut into several launches of at most ZR_LAUNCH_BYTES
+// of traffic each.  Within one launch the eight XCDs take every eighth tile in
+// dispatch order but run at different speeds (measured: some ~10% slower than
+// others), so in a long launch they drift apart -- by 140k tiles, 290 MB of
+// every stream, late in a 10 ms launch -- the addresses in flight spread over
+// a widening window, and the launch ends on the slowest XCD.  A kernel
+// boundary brings them back together.  Measured on the fused fp32 8-replica
+// step over a 1.0e9-element share: 5.88 TB/s as one launch, 6.06 TB/s in
+// launches of 2 GiB (interleaved in one process).  Every kernel therefore
+// takes a tile range [tile_base, tile_end) in its arguments.
+//
 // Arithmetic follows the method's definition exactly: each replica's value is
 // divided by D first, the quotients are summed in rank order 0..R-1 starting
 // from the rank-0 quotient, every operation is a separate fp32 operation
@@ -313,7 +324,8 @@ struct RedArgs {
   uint64_t in[ZR_MAX_WORLD];   // replica r's flat element f: in[r] + f*sizeof
   uint64_t out[ZR_MAX_WORLD];  // reduce mode: partition d's element j: out[d] + 4j
   const Seg* segs;
-  int64_t total_tiles;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end)
+  int64_t tile_end;
   int32_t nseg;
   int32_t R;
   float divisor;
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
 
-  for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     Seg sg;
     if constexpr (kArgSegs)
       sg = a.aseg[find_arg_seg(a.aseg, a.nseg, t)];
@@ -680,6 +692,8 @@ struct AdamArgs {
   float* v;
   uint16_t* pbf16;
   int64_t n;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end)
+  int64_t tile_end;
   AdamConsts ac;
 };
 
@@ -690,8 +704,7 @@ template <bool kVec, bool kDword>
 __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
   using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
-  const int64_t ntiles = (a.n + kAdamTileElems - 1) / kAdamTileElems;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const uint64_t t4 = static_cast<uint64_t>(t) * kAdamTileElems * 4;
     const uint64_t b_g = reinterpret_cast<uint64_t>(a.grad) + t4;
     const uint64_t b_master = reinterpret_cast<uint64_t>(a.master) + t4;
@@ -746,7 +759,8 @@ struct IpgSeg {
 
 struct IpgArgs {
   IpgSeg seg[kIpgMaxSegs];
-  int64_t total_tiles;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end)
+  int64_t tile_end;
   float* main_grad;
   int32_t nseg;
 };
@@ -758,7 +772,7 @@ struct IpgArgs {
 template <typename InT, bool kDword>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
   using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
-  for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const IpgSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
     const uint64_t mg = reinterpret_cast<uint64_t>(a.main_grad);
@@ -828,7 +842,8 @@ struct CopyArgs {
   const float* src;  // bucket-layout source
   float* dst;        // partition
   const Seg* segs;   // flat = bucket offset, part = partition offset
-  int64_t total_tiles;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end)
+  int64_t tile_end;
   int32_t nseg;
 };
 
@@ -838,7 +853,7 @@ struct CopyArgs {
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
-  for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
     const float* s = a.src + sg.flat;
@@ -881,6 +896,8 @@ struct RingArgs {
   uint64_t buf[ZR_MAX_WORLD];
   int64_t chunk;
   int64_t tiles_per_rank;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end) of
+  int64_t tile_end;   // tiles_per_rank * n
   int32_t n;
   int32_t step;
 };
@@ -888,8 +905,7 @@ struct RingArgs {
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
-  const int64_t total = a.tiles_per_rank * a.n;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
     const int64_t lt = t - static_cast<int64_t>(k) * a.tiles_per_rank;
     int c = (k - a.step - 2) % a.n;
@@ -948,7 +964,8 @@ struct XSeg {
 
 struct XArgs {
   XSeg seg[kXMaxSegs];
-  int64_t total_tiles;
+  int64_t tile_base;  // this launch's tiles: [tile_base, tile_end)
+  int64_t tile_end;
   int32_t nseg;
 };
 
@@ -974,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
   constexpr int64_t TE = gather_tile_elems<T>();       // elements per tile
   constexpr int GS = static_cast<int>(TE / (kThreads * GV));
   static_assert(GS >= 1 && TE == int64_t(GS) * kThreads * GV, "gather tile shape");
-  for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const XSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
     int j0 = -1;
@@ -1030,8 +1047,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
   using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
-  const int64_t total = a.tiles_per_rank * a.n;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
     const int64_t lt = t - static_cast<int64_t>(k) * a.tiles_per_rank;
     int c = (k - a.step - 1) % a.n;
@@ -1152,6 +1168,24 @@ unsigned grid_for(int64_t tiles, int cus) {
                                          : int64_t(1) << 30;
   return static_cast<unsigned>(std::max<int64_t>(1, std::min(tiles, cap)));
 }
+
+// Traffic one launch should carry at most (the file comment says why long
+// launches are cut).  A/B-measured, launches interleaved in one process: on
+// the 1.0e9-element fp32 8-replica fused share 1 GiB 6.02, 2 GiB 6.06, 4 GiB
+// 6.05, uncut 5.88 TB/s; on the 5.4e8-element 2-replica MoE expert share
+// 5.99 / 6.08 / 6.11 / 6.10 TB/s.
+#ifndef ZR_LAUNCH_BYTES
+#define ZR_LAUNCH_BYTES (int64_t(2) << 30)
+#endif
+
+// Number of equal launches that cover `total` tiles of `tile_bytes` bytes of
+// algorithmic traffic each, every launch carrying at most ~ZR_LAUNCH_BYTES.
+int64_t launches_for(int64_t total, int64_t tile_bytes) {
+  const int64_t per = std::max<int64_t>(1, int64_t(ZR_LAUNCH_BYTES) / std::max<int64_t>(1, tile_bytes));
+  return std::max<int64_t>(1, (total + per - 1) / per);
+}
+// Tiles [first, end) of launch i of n over `total` tiles.
+int64_t launch_first(int64_t total, int64_t n, int64_t i) { return total * i / n; }
 
 // Segments of `group`, `bucket` (-1 all), `dst` (-1 all) in bucket order, plus
 // the padding of the selected partitions when the call covers the last bucket
@@ -1386,13 +1420,11 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
   if (st != ZR_OK) return st;
-  st = get_dev_table(plan, kReduceTable, group, bucket, dst, device, *hs, &a.segs);
-  if (st != ZR_OK) return st;
   for (int r = 0; r < gi.world; ++r)
     a.in[r] = reinterpret_cast<uint64_t>(reps[r].ptr) -
               static_cast<uint64_t>(reps[r].flat_base) * s;
   a.nseg = nseg;
-  a.total_tiles = (*hs)[nseg].tile0;
+  const int64_t total = (*hs)[nseg].tile0;
   a.R = gi.world;
   a.divisor = static_cast<float>(gi.divisor);
   a.inv_divisor = 1.0f / static_cast<float>(gi.divisor);
@@ -1424,23 +1456,43 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   };
   bool dword = false;
   for (int i = 0; i < nseg && !dword; ++i) dword = !slot_phase_exists((*hs)[i]);
-  // A capped grid walks the tiles in steps of its size (the kernel's
-  // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
-  const unsigned grid = max_wgs > 0
-      ? static_cast<unsigned>(std::min<int64_t>(grid_for(a.total_tiles, cus), max_wgs))
-      : grid_for(a.total_tiles, cus);
-  // Mid-sized selections of few segments carry their segments in the kernel
-  // arguments (short launches measured faster with the device table).
+  // Bytes one tile moves (the replicas, plus the partition output or the
+  // Adam state), which sets how many launches the selection is cut into.
+  const int64_t tile_bytes =
+      kTileElems * (static_cast<int64_t>(gi.world) * static_cast<int64_t>(s) +
+                    (fused ? 26 + (gout ? 4 : 0) : 4));
+  const int64_t nl = launches_for(total, tile_bytes);
+  const int64_t per = (total + nl - 1) / nl;
+  // Mid-sized launches over few segments carry their segments in the kernel
+  // arguments (short launches measured faster with the device table); only
+  // the other calls need the device table.
+  const bool argsegs = !dword && nseg <= kRedArgSegs && per >= kRedArgSegsMinTiles &&
+                       per <= kRedArgSegsMaxTiles;
+  if (!argsegs) {
+    st = get_dev_table(plan, kReduceTable, group, bucket, dst, device, *hs, &a.segs);
+    if (st != ZR_OK) return st;
+  }
   RedArgsS as;
   static_cast<RedArgs&>(as) = a;
-  const bool argsegs = !dword && nseg <= kRedArgSegs && a.total_tiles >= kRedArgSegsMinTiles &&
-                       a.total_tiles <= kRedArgSegsMaxTiles;
   for (int i = 0; i < kRedArgSegs; ++i) as.aseg[i] = i < nseg ? (*hs)[i] : Seg{};
-  if (dt == ZR_BF16)
-    return fused ? launch_reduce_t<uint16_t, true>(as, gi.world, div, dword, argsegs, grid, stream)
+  for (int64_t i = 0; i < nl; ++i) {
+    as.tile_base = launch_first(total, nl, i);
+    as.tile_end = launch_first(total, nl, i + 1);
+    // A capped grid walks the tiles in steps of its size (the kernel's
+    // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
+    const int64_t n = as.tile_end - as.tile_base;
+    const unsigned grid = max_wgs > 0
+        ? static_cast<unsigned>(std::min<int64_t>(grid_for(n, cus), max_wgs))
+        : grid_for(n, cus);
+    if (dt == ZR_BF16)
+      st = fused ? launch_reduce_t<uint16_t, true>(as, gi.world, div, dword, argsegs, grid, stream)
                  : launch_reduce_t<uint16_t, false>(as, gi.world, div, dword, argsegs, grid, stream);
-  return fused ? launch_reduce_t<float, true>(as, gi.world, div, dword, argsegs, grid, stream)
-               : launch_reduce_t<float, false>(as, gi.world, div, dword, argsegs, grid, stream);
+    else
+      st = fused ? launch_reduce_t<float, true>(as, gi.world, div, dword, argsegs, grid, stream)
+                 : launch_reduce_t<float, false>(as, gi.world, div, dword, argsegs, grid, stream);
+    if (st != ZR_OK) return st;
+  }
+  return ZR_OK;
 }
 
 }  // namespace
@@ -1521,11 +1573,19 @@ extern "C" zr_status zr_adam_partition(const zr_adam* h, const float* grad, floa
   // fp32 pointers are always dword-aligned; the bf16 output must be too
   // for its 8-byte stores (an even element offset).
   const bool dword = !param_bf16 || elem_aligned(param_bf16, 4);
-  const unsigned grid = grid_for((n + kAdamTileElems - 1) / kAdamTileElems, cus);
-  if (vec) adam_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
-  else if (dword) adam_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
-  else adam_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
-  return check_launch("adam_partition launch");
+  const int64_t total = (n + kAdamTileElems - 1) / kAdamTileElems;
+  const int64_t nl = launches_for(total, kAdamTileElems * 30);
+  for (int64_t i = 0; i < nl; ++i) {
+    a.tile_base = launch_first(total, nl, i);
+    a.tile_end = launch_first(total, nl, i + 1);
+    const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+    if (vec) adam_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+    else if (dword) adam_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
+    else adam_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+    st = check_launch("adam_partition launch");
+    if (st != ZR_OK) return st;
+  }
+  return ZR_OK;
 }
 
 extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param_ids,
@@ -1583,9 +1643,7 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
         tiles += tiles_for(segs[i].numel, kIpgTileElems);
       }
       a.nseg = static_cast<int32_t>(e - b);
-      a.total_tiles = tiles;
       a.main_grad = main_grad;
-      const unsigned grid = grid_for(tiles, cus);
       // The dword-aligned variant is needed when some segment has no phase
       // at which the gradient and main_grad are both slot-aligned.
       bool dword = false;
@@ -1597,15 +1655,21 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
                 aligned(mgp + static_cast<uint64_t>(a.seg[i].dst + j) * 4, 16);
         dword = !any;
       }
-      if (grad_dtype == ZR_BF16) {
-        if (dword) ipg_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
-        else ipg_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
-      } else {
-        if (dword) ipg_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
-        else ipg_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+      const int64_t nl = launches_for(tiles, kIpgTileElems * static_cast<int64_t>(s + 8));
+      for (int64_t i = 0; i < nl; ++i) {
+        a.tile_base = launch_first(tiles, nl, i);
+        a.tile_end = launch_first(tiles, nl, i + 1);
+        const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+        if (grad_dtype == ZR_BF16) {
+          if (dword) ipg_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
+          else ipg_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+        } else {
+          if (dword) ipg_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
+          else ipg_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+        }
+        st = check_launch("ipg_accumulate launch");
+        if (st != ZR_OK) return st;
       }
-      st = check_launch("ipg_accumulate launch");
-      if (st != ZR_OK) return st;
     }
     return ZR_OK;
   } catch (...) {
@@ -1643,7 +1707,7 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
     a.src = bucket_layout_src;
     a.dst = part_out;
     a.nseg = nseg;
-    a.total_tiles = (*hs)[nseg].tile0;
+    const int64_t total = (*hs)[nseg].tile0;
     // The dword-aligned variant is needed when some segment has no phase at
     // which source and destination are both 16-byte aligned.
     bool dword = false;
@@ -1654,9 +1718,17 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
       for (uint64_t j = 0; j < VE && !any; ++j) any = aligned(sa + 4 * j, 16) && aligned(da + 4 * j, 16);
       dword = !any;
     }
-    if (dword) copy_kernel<true><<<grid_for(a.total_tiles, cus), kThreads, 0, stream>>>(a);
-    else copy_kernel<false><<<grid_for(a.total_tiles, cus), kThreads, 0, stream>>>(a);
-    return check_launch("copy_grads_in_partition launch");
+    const int64_t nl = launches_for(total, kCopyTileElems * 8);
+    for (int64_t i = 0; i < nl; ++i) {
+      a.tile_base = launch_first(total, nl, i);
+      a.tile_end = launch_first(total, nl, i + 1);
+      const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+      if (dword) copy_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+      else copy_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+      st = check_launch("copy_grads_in_partition launch");
+      if (st != ZR_OK) return st;
+    }
+    return ZR_OK;
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1702,7 +1774,6 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
       tiles += (g.numel + 16 / static_cast<int64_t>(es) - 1 + te - 1) / te;
     }
     a.nseg = n;
-    a.total_tiles = tiles;
     int device = 0, cus = 1;
     zr_status st = device_info(&device, &cus);
     if (st != ZR_OK) return st;
@@ -1715,15 +1786,22 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
         any = aligned(a.seg[i].src + j * es, 16) && aligned(a.seg[i].dst + j * es, 16);
       dword = !any;
     }
-    const unsigned grid = grid_for(tiles, cus);
-    if (dtype == ZR_BF16) {
-      if (dword) gather_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
-      else gather_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
-    } else {
-      if (dword) gather_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
-      else gather_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+    const int64_t nl = launches_for(tiles, kGatherTileBytes * 2);
+    for (int64_t i = 0; i < nl; ++i) {
+      a.tile_base = launch_first(tiles, nl, i);
+      a.tile_end = launch_first(tiles, nl, i + 1);
+      const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+      if (dtype == ZR_BF16) {
+        if (dword) gather_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
+        else gather_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+      } else {
+        if (dword) gather_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
+        else gather_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+      }
+      st = check_launch("all_gather_params launch");
+      if (st != ZR_OK) return st;
     }
-    return check_launch("all_gather_params launch");
+    return ZR_OK;
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1784,10 +1862,19 @@ extern "C" zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
   if (st != ZR_OK) return st;
-  const unsigned grid = grid_for(a.tiles_per_rank * n_ranks, cus);
-  if (ring_needs_dword(a, 1)) ring_ag_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-  else ring_ag_kernel<false><<<grid, kThreads, 0, stream>>>(a);
-  return check_launch("ring_ag_step launch");
+  const bool dword = ring_needs_dword(a, 1);
+  const int64_t total = a.tiles_per_rank * n_ranks;
+  const int64_t nl = launches_for(total, kRingAgTileElems * 8);
+  for (int64_t i = 0; i < nl; ++i) {
+    a.tile_base = launch_first(total, nl, i);
+    a.tile_end = launch_first(total, nl, i + 1);
+    const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+    if (dword) ring_ag_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+    else ring_ag_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+    st = check_launch("ring_ag_step launch");
+    if (st != ZR_OK) return st;
+  }
+  return ZR_OK;
 }
 
 extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
@@ -1800,8 +1887,17 @@ extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
   if (st != ZR_OK) return st;
-  const unsigned grid = grid_for(a.tiles_per_rank * n_ranks, cus);
-  if (ring_needs_dword(a, 2)) ring_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-  else ring_kernel<false><<<grid, kThreads, 0, stream>>>(a);
-  return check_launch("ring_rs_step launch");
+  const bool dword = ring_needs_dword(a, 2);
+  const int64_t total = a.tiles_per_rank * n_ranks;
+  const int64_t nl = launches_for(total, kRingTileElems * 12);
+  for (int64_t i = 0; i < nl; ++i) {
+    a.tile_base = launch_first(total, nl, i);
+    a.tile_end = launch_first(total, nl, i + 1);
+    const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
+    if (dword) ring_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+    else ring_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+    st = check_launch("ring_rs_step launch");
+    if (st != ZR_OK) return st;
+  }
+  return ZR_OK;
 }

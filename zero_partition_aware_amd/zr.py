@@ -219,6 +219,24 @@ def _padded_numel(plan, group):
     return L
 
 
+def _world(plan, group):
+    """R_g of the plan's group (L_g / P_g), queried once per plan and group."""
+    key = ("world", group)
+    R = plan.part_numel.get(key)
+    if R is None:
+        _, L, P, _ = zr_plan_group_info(plan, group)
+        R = plan.part_numel[key] = L // P
+    return R
+
+
+def _expect_len(seq, n, name):
+    """The C calls index host arrays by rank: a list shorter (or longer) than
+    the group needs would make them read past the array, so its length is
+    checked here."""
+    if len(seq) != n:
+        raise ZrError(ZR_ERR_INVALID, f"{name} has {len(seq)} entries; the call needs {n}")
+
+
 def _dtype_code(t):
     dt = t.dtype
     if dt is torch.bfloat16:
@@ -244,9 +262,10 @@ def _adam(lr, beta1, beta2, eps, step):
 class Plan:
     """Owns a zr_plan handle (freed with zr_plan_free)."""
 
-    def __init__(self, handle):
+    def __init__(self, handle, numels=()):
         self._h = handle
         self.part_numel = {}      # group -> P_g (the plan is immutable)
+        self.numels = tuple(int(n) for n in numels)   # param sizes, list order
 
     @property
     def handle(self):
@@ -282,7 +301,7 @@ def zr_plan_buckets(numels, param_groups, groups, reduce_bucket_size,
                                 _i32(partition_gradients, "partition_gradients"),
                                 _i64(align, "align"),
                                 ctypes.byref(out)))
-    return Plan(out.value)
+    return Plan(out.value, numels)
 
 
 def zr_plan_free(plan):
@@ -361,15 +380,23 @@ def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
         raise ZrError(ZR_ERR_INVALID, "param_ids and grads differ in length")
     ids = (c_i64 * max(n, 1))(*[_i64(p, f"param_ids[{i}]") for i, p in enumerate(param_ids)])
     dt = _dtype_code(grads[0]) if n else ZR_FP32
-    ptrs = (c_vp * max(n, 1))(*[_buf(g, f"grads[{i}]", dt).value for i, g in enumerate(grads)])
+
+    def need(i):
+        # the param's size; an out-of-range id is left to the C call's check
+        p = ids[i]
+        return plan.numels[p] if 0 <= p < len(plan.numels) else None
+
+    ptrs = (c_vp * max(n, 1))(*[_buf(g, f"grads[{i}]", dt, need(i)).value
+                                for i, g in enumerate(grads)])
     wl = main_grad.numel() if window_len is None else _i64(window_len, "window_len")
     _check(_lib.zr_ipg_accumulate(plan.handle, ids, ptrs, n, dt,
                                   _buf(main_grad, "main_grad", ZR_FP32, wl),
                                   _i64(window_base, "window_base"), wl, _stream(stream)))
 
 
-def _replicas(reps):
-    """reps: list of tensors (flat_base 0) or (tensor, flat_base) pairs."""
+def _replicas(reps, plan, group):
+    """reps: list of R_g tensors (flat_base 0) or (tensor, flat_base) pairs."""
+    _expect_len(reps, _world(plan, group), "reps")
     arr = (zr_replica * max(len(reps), 1))()
     dt = None
     for i, r in enumerate(reps):
@@ -384,8 +411,11 @@ def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
                             stream=None):
     """part_out: list of fp32 tensors (all destinations when dst == -1, else
     the one partition)."""
-    arr, dt = _replicas(reps)
+    arr, dt = _replicas(reps, plan, group)
     P = _part_numel(plan, group)
+    R = _world(plan, group)
+    if -1 <= _i32(dst, "dst") < R:        # an out-of-range dst is the C call's error
+        _expect_len(part_out, R if int(dst) == -1 else 1, "part_out")
     outs = (c_vp * max(len(part_out), 1))(
         *[_buf(t, f"part_out[{i}]", ZR_FP32, P).value if t is not None else None
           for i, t in enumerate(part_out)])
@@ -422,7 +452,7 @@ def zr_adam_partition(grad, master, m, v, param_bf16=None, lr=1e-3, beta1=0.9,
 def zr_reduce_scatter_adam(plan, group, bucket, dst, reps, master, m, v,
                            param_bf16=None, grad_out=None, lr=1e-3, beta1=0.9,
                            beta2=0.999, eps=1e-8, step=1, stream=None):
-    arr, dt = _replicas(reps)
+    arr, dt = _replicas(reps, plan, group)
     h = _adam(lr, beta1, beta2, eps, step)
     # dst == -1: the state buffers hold every partition (L_g elements)
     P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
@@ -440,7 +470,7 @@ def zr_reduce_scatter_adam_capped(plan, group, bucket, dst, reps, master, m, v,
                                   param_bf16=None, grad_out=None, max_workgroups=256,
                                   lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=1,
                                   stream=None):
-    arr, dt = _replicas(reps)
+    arr, dt = _replicas(reps, plan, group)
     h = _adam(lr, beta1, beta2, eps, step)
     P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
     _check(_lib.zr_reduce_scatter_adam_capped(plan.handle, _i32(group, "group"),
@@ -468,7 +498,7 @@ class PreparedReduceScatterAdam:
                  grad_out=None, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
                  max_workgroups=0):
         self._keep = (plan, list(reps), master, m, v, param_bf16, grad_out)
-        self._arr, self._dt = _replicas(reps)
+        self._arr, self._dt = _replicas(reps, plan, group)
         self._group = _i32(group, "group")
         self._dst = _i32(dst, "dst")
         P = _part_numel(plan, group) if self._dst >= 0 else _padded_numel(plan, group)
@@ -526,6 +556,7 @@ def zr_all_gather_params(plan, group, parts, out, out_base=0, out_len=None,
     """parts: list of R_g partition tensors (bf16 or fp32); out: tensor that
     receives flat elements [out_base, out_base + out_len)."""
     n = len(parts)
+    _expect_len(parts, _world(plan, group), "parts")
     dt = _dtype_code(out)
     P = _part_numel(plan, group)
     arr = (c_vp * max(n, 1))(*[(_buf(t, f"parts[{i}]", dt, P).value if t is not None else 0)
