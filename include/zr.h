@@ -288,6 +288,30 @@ zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t group,
                                         float* grad_out, int32_t max_workgroups,
                                         hipStream_t stream);
 
+/* zr_reduce_scatter_adam_noalloc -- zr_reduce_scatter_adam for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors, bit for bit; it allocates no device memory.  Where
+ * zr_reduce_scatter_adam uploads the selection's segment table into memory
+ * the library allocates (once per selection), this call stages the table on
+ * `stream` before its reduce launches, into a fixed device array of 256 KiB
+ * that the library holds on each GPU for the life of the process: at most
+ * 6,552 segments per selection, else ZR_ERR_INVALID before anything is
+ * enqueued.  (A selection's segments are its merged slices plus one padding
+ * segment per selected partition; selections of at most two segments whose
+ * launches span 16K-256K tiles need no table at all.)  Every call on one GPU
+ * shares that GPU's array and leaves its own table there, so calls that
+ * overlap on one GPU -- on different streams without an ordering between
+ * them -- race: order them on one stream or with events.  The plan's
+ * host-side segment list for a selection is still built on its first use
+ * (host memory). */
+zr_status zr_reduce_scatter_adam_noalloc(const zr_plan* plan, int32_t group,
+                                         int64_t bucket, int32_t dst,
+                                         const zr_replica* reps, zr_dtype grad_dtype,
+                                         const zr_adam* h, float* master, float* m,
+                                         float* v, uint16_t* param_bf16,
+                                         float* grad_out, hipStream_t stream);
+
 /* zr_ring_rs_step -- one step of ring reduce-scatter with every card's buffer
  * resident in this GPU ([Megatron DP] "深入：all-reduce 底层算法（NCCL）", ring
  * reduce-scatter phase).  rank_bufs[n_ranks] (host array of device fp32

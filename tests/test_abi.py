@@ -230,6 +230,17 @@ def test_binding_checks_list_lengths_against_the_group():
         zr.zr_all_gather_params(plan, 0, [buf] * 3, whole, stream=0)
 
 
+def test_noalloc_rejects_tables_beyond_its_array():
+    """The no-allocation call stages at most 6,552 segments: a selection with
+    more is refused before anything touches a GPU."""
+    plan = zr.zr_plan_buckets([1] * 7000, [0] * 7000, [(1, 1)], 1)   # 7000 one-element slices
+    reps = [_FakeTensor(0x1000, 7000)]
+    buf = _FakeTensor(0x100000, 7000)
+    with pytest.raises(zr.ZrError, match="7000 segments; the no-allocation call stages at most 6552") as ei:
+        zr.zr_reduce_scatter_adam_noalloc(plan, 0, -1, -1, reps, buf, buf, buf, stream=0)
+    assert ei.value.status == zr.ZR_ERR_INVALID
+
+
 def test_ring_rejects_bad_step_and_overlap():
     bufs = [_FakeTensor(0x100000 * (i + 1), 8 * 16) for i in range(8)]
     with pytest.raises(zr.ZrError, match="step"):

@@ -64,6 +64,15 @@
 
 using zr::fail;
 
+// The no-allocation entry point's staging buffer: its launch tables (at most
+// kScratchBytes, i.e. 6,552 segments) are written here by a staging kernel on
+// the caller's stream, then read by the reduce kernel.  Each GPU holds its own
+// copy for the life of the process.  Host code never uses this name as a
+// device address (on the host it is a stand-in, not the array): it uses the
+// per-device address from hipGetSymbolAddress (scratch_for below).
+constexpr size_t kScratchBytes = 256 * 1024;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 // Launch-shape constants (compile-time; the defaults are the tuned values).
@@ -353,6 +362,21 @@ constexpr int64_t kRedArgSegsMaxTiles = 262144;
 struct RedArgsS : RedArgs {
   Seg aseg[kRedArgSegs];
 };
+
+// Segment tables of the no-allocation entry point are staged in a
+// file-scope device array (`scratch`, below) instead of memory the library
+// allocates.  A staging launch copies up to kStageSegs segments from its
+// kernel arguments into the array, one segment per lane.
+constexpr int kStageSegs = 64;
+struct StageArgs {
+  Seg seg[kStageSegs];
+  Seg* out;  // scratch address of the first segment this launch writes
+  int32_t n;
+};
+__global__ __launch_bounds__(kStageSegs) void stage_segs_kernel(const StageArgs a) {
+  const int i = static_cast<int>(threadIdx.x);
+  if (i < a.n) a.out[i] = a.seg[i];
+}
 
 template <bool kDiv>
 __device__ __forceinline__ float predivide(const RedArgs& a, float x) {
@@ -1349,13 +1373,52 @@ zr_status launch_reduce_t(const RedArgsS& as, int R, bool div, bool dword, bool 
   return check_launch(kFused ? "reduce_scatter_adam launch" : "reduce_scatter launch");
 }
 
+// Largest segment table (sentinel excluded) the no-allocation call stages.
+constexpr int64_t kScratchSegs = static_cast<int64_t>(kScratchBytes / sizeof(Seg)) - 1;
+static_assert(sizeof(Seg) == 40 && kScratchSegs == 6552, "scratch capacity stated in the header");
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+zr_status scratch_for(int device, Seg** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(ZR_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = static_cast<Seg*>(g_scratch_ptr[device]);
+  return ZR_OK;
+}
+
+// Writes segs[0, n) into the scratch table on `stream` (vector stores from a
+// staging kernel; nothing allocated).
+zr_status stage_segments(const Seg* segs, int64_t n, Seg* table, hipStream_t stream) {
+  for (int64_t b = 0; b < n; b += kStageSegs) {
+    StageArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.n = static_cast<int32_t>(std::min<int64_t>(kStageSegs, n - b));
+    for (int i = 0; i < sa.n; ++i) sa.seg[i] = segs[b + i];
+    sa.out = table + b;
+    stage_segs_kernel<<<1, kStageSegs, 0, stream>>>(sa);
+    const zr_status st = check_launch("segment staging launch");
+    if (st != ZR_OK) return st;
+  }
+  return ZR_OK;
+}
+
 // Shared validation + launch of the reduce kernel in either mode; max_wgs > 0
-// caps the grid (0: one workgroup per tile).
+// caps the grid (0: one workgroup per tile).  noalloc: the segment table is
+// staged in `scratch` instead of the plan's device table.
 zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t dst,
                      const zr_replica* reps, zr_dtype dt, float* const* part_out,
                      const zr_adam* h, float* master, float* m, float* v,
                      uint16_t* pbf16, float* gout, bool fused, int64_t max_wgs,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool noalloc = false) {
   zr::clear_error();
   if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
   if (group < 0 || group >= static_cast<int32_t>(plan->groups.size()))
@@ -1416,6 +1479,10 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
                                         std::to_string(g.flat) + ", " +
                                         std::to_string(g.flat + g.numel) + ")");
   }
+  if (noalloc && nseg > kScratchSegs)
+    return fail(ZR_ERR_INVALID, "the selection has " + std::to_string(nseg) +
+                                    " segments; the no-allocation call stages at most " +
+                                    std::to_string(kScratchSegs));
   if (nseg == 0) return ZR_OK;
   int device = 0, cus = 1;
   st = device_info(&device, &cus);
@@ -1468,7 +1535,14 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   // the other calls need the device table.
   const bool argsegs = !dword && nseg <= kRedArgSegs && per >= kRedArgSegsMinTiles &&
                        per <= kRedArgSegsMaxTiles;
-  if (!argsegs) {
+  if (!argsegs && noalloc) {
+    Seg* table = nullptr;
+    st = scratch_for(device, &table);
+    if (st != ZR_OK) return st;
+    st = stage_segments(hs->data(), nseg + 1, table, stream);
+    if (st != ZR_OK) return st;
+    a.segs = table;
+  } else if (!argsegs) {
     st = get_dev_table(plan, kReduceTable, group, bucket, dst, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
@@ -1540,6 +1614,21 @@ extern "C" zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t 
     }
     return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
                       v, param_bf16, grad_out, true, max_workgroups, stream);
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
+
+extern "C" zr_status zr_reduce_scatter_adam_noalloc(const zr_plan* plan, int32_t group,
+                                                    int64_t bucket, int32_t dst,
+                                                    const zr_replica* reps,
+                                                    zr_dtype grad_dtype, const zr_adam* h,
+                                                    float* master, float* m, float* v,
+                                                    uint16_t* param_bf16, float* grad_out,
+                                                    hipStream_t stream) {
+  try {
+    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
+                      v, param_bf16, grad_out, true, 0, stream, true);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }

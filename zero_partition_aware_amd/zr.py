@@ -108,6 +108,9 @@ _sigs = {
     "zr_reduce_scatter_adam_capped": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
                                               c_i32, _P(zr_adam), c_vp, c_vp, c_vp, c_vp,
                                               c_vp, c_i32, c_vp]),
+    "zr_reduce_scatter_adam_noalloc": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
+                                               c_i32, _P(zr_adam), c_vp, c_vp, c_vp, c_vp,
+                                               c_vp, c_vp]),
     "zr_ring_rs_step": (c_i32, [_P(c_vp), c_i32, c_i64, c_i32, c_vp]),
     "zr_ring_ag_step": (c_i32, [_P(c_vp), c_i32, c_i64, c_i32, c_vp]),
     "zr_all_gather_params": (c_i32, [c_vp, c_i32, _P(c_vp), c_i32, c_vp, c_i64, c_i64,
@@ -483,6 +486,26 @@ def zr_reduce_scatter_adam_capped(plan, group, bucket, dst, reps, master, m, v,
                                               _buf(grad_out, "grad_out", ZR_FP32, P),
                                               _i32(max_workgroups, "max_workgroups"),
                                               _stream(stream)))
+
+
+def zr_reduce_scatter_adam_noalloc(plan, group, bucket, dst, reps, master, m, v,
+                                   param_bf16=None, grad_out=None, lr=1e-3, beta1=0.9,
+                                   beta2=0.999, eps=1e-8, step=1, stream=None):
+    """zr_reduce_scatter_adam without device allocation: the segment table is
+    staged in the library's fixed per-GPU array (calls that overlap on one GPU
+    race)."""
+    arr, dt = _replicas(reps, plan, group)
+    h = _adam(lr, beta1, beta2, eps, step)
+    P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
+    _check(_lib.zr_reduce_scatter_adam_noalloc(plan.handle, _i32(group, "group"),
+                                               _i64(bucket, "bucket"), _i32(dst, "dst"), arr,
+                                               dt, ctypes.byref(h),
+                                               _buf(master, "master", ZR_FP32, P),
+                                               _buf(m, "m", ZR_FP32, P),
+                                               _buf(v, "v", ZR_FP32, P),
+                                               _buf(param_bf16, "param_bf16", ZR_BF16, P),
+                                               _buf(grad_out, "grad_out", ZR_FP32, P),
+                                               _stream(stream)))
 
 
 class PreparedReduceScatterAdam:
