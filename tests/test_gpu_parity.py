@@ -9,6 +9,7 @@ import pytest
 
 from oracle.adam import adam_oracle
 from oracle.bf16 import bf16_rne_oracle
+from oracle.copy import bucket_layout_mean, copy_grads_in_partition_oracle
 from oracle.ipg import ipg_accumulate_oracle
 from oracle.plan import plan_oracle
 from oracle.reduce import reduce_scatter_oracle
@@ -471,26 +472,32 @@ def test_ring_integer_equals_direct_sum():
 
 
 def test_copy_grads_in_partition():
+    """Standalone copy into the partition against the copy oracle, on a
+    shrunken MoE-like list (interleaved groups, many small buckets): the
+    bucket-layout source is the oracle's reduced bucket, so the copied
+    partition also equals the oracle's reduce-scatter of that bucket."""
     w = workloads.get("moe-16l")
-    # a shrunken MoE-like list: interleaved groups, many small buckets
     numels = [n // 4096 + 1 for n in w.numels[:34]]
     pg = w.param_groups[:34]
     ref = plan_oracle(numels, pg, w.groups, 3000)
     plan = zr.zr_plan_buckets(numels, pg, w.groups, 3000)
     rng = np.random.default_rng(1)
+    reps = [[rng.standard_normal(g.total).astype(np.float32) for _ in range(g.world)]
+            for g in ref.groups]
     for b in range(ref.num_buckets):
-        src = rng.standard_normal(3000).astype(np.float32)
+        src = np.zeros(3000, np.float32)
+        lay = bucket_layout_mean(ref, b, reps, False)
+        src[:lay.size] = lay
         dsrc = to_dev(src, b % 2)
         for g, info in enumerate(ref.groups):
             for k in range(info.world):
                 out = empty_f32(info.part_numel)
                 zr.zr_copy_grads_in_partition(plan, g, b, k, dsrc, out)
-                want = np.full(info.part_numel, np.nan, np.float32)
-                for s in ref.slices:
-                    if s.bucket == b and s.group == g and s.dst == k:
-                        want[s.part_offset:s.part_offset + s.numel] = \
-                            src[s.bucket_offset:s.bucket_offset + s.numel]
+                want = copy_grads_in_partition_oracle(ref, g, b, k, src)
                 assert_bits_equal(host_f32(out), want, f"bucket {b} group {g} dst {k}")
+                rs = reduce_scatter_oracle(ref, g, reps[g], False, bucket=b, dst=k)[k]
+                sel = ~np.isnan(want)
+                assert_bits_equal(host_f32(out)[sel], rs[sel], f"bucket {b} group {g} dst {k} vs RS")
 
 
 def test_invalid_call_leaves_outputs_untouched():

@@ -1,6 +1,8 @@
-"""HIP path at the workloads' full sizes, checked on sampled outputs that the
-oracle computes one by one from the gathered inputs (bit-exact for reduced
-gradients and IPG sums, within rel 1e-6 / abs 1e-7 for Adam)."""
+"""HIP path at the workloads' full sizes: every element of every GPT-2 partition
+and of Llama-3-8B rank 0's whole share against the oracle, and sampled outputs
+that the oracle computes one by one for the IPG fills, the MoE groups and the
+ring (bit-exact for reduced gradients and IPG sums, within rel 1e-6 / abs 1e-7
+for Adam)."""
 
 import gc
 
@@ -67,35 +69,52 @@ def _widen(u16):
     return (u16.astype(np.uint32) << 16).view(np.float32)
 
 
+def _check_full(xs, is_bf16, D, th, master, m, v, pbf16, gout, what):
+    """Every element of one partition against the oracle (reduced gradient
+    bit-exact, Adam in tolerance, bf16 = RNE of the kernel's master)."""
+    want_g = rank_order_mean([(_widen(x) if is_bf16 else x) for x in xs], D)
+    assert_bits_equal(host_f32(gout), want_g, f"{what}: reduced gradient")
+    z = np.zeros_like(th)
+    w_th, w_m, w_v = adam_oracle(want_g, th, z, z, step=1, **HP)
+    g_th = host_f32(master)
+    assert_within(g_th, w_th, what=f"{what}: master")
+    assert_within(host_f32(m), w_m, what=f"{what}: m")
+    assert_within(host_f32(v), w_v, atol=0.0, what=f"{what}: v")
+    assert np.array_equal(host_u16(pbf16), bf16_rne_oracle(g_th)), f"{what}: bf16 param"
+
+
 def test_gpt2_small_fused_every_rank():
+    """Every rank's fused step on its own state, every element of every
+    partition against the oracle.  GPT-2's total is 8 x 15,554,976: every
+    partition is one slice of the single bucket."""
     name = "gpt2-small"
     w = workloads.get(name)
     ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
     plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
     info = ref.groups[0]
     T, P, R = info.total, info.part_numel, info.world
+    assert T == R * P and all(s.numel == P for s in ref.slices)
     reps = [workloads.device_normal(workloads.seed_for(name, r), T, w.grad_sigma, DEV, "bf16")
             for r in range(R)]
     for k in range(R):
         master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
                                          w.master_sigma, DEV)
-        idx = _sample(P, 20000, k, [s for s in ref.slices if s.dst == k])
-        th_s = _gather(master, idx)
+        th = host_f32(master)
         m = torch.zeros(P, device=DEV)
         v = torch.zeros(P, device=DEV)
         pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
         gout = torch.empty(P, device=DEV)
         zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, master, m, v, pbf16, gout, **HP)
-        reps_s = [_gather(r_, k * P + idx) for r_ in reps]
-        _check_fused(reps_s, True, info.divisor, th_s, master, m, v, pbf16, gout, idx)
-        print(f"gpt2-small rank {k}: {idx.size} sampled elements ok")
+        xs = [host_u16(r_[k * P:(k + 1) * P]) for r_ in reps]
+        _check_full(xs, True, info.divisor, th, master, m, v, pbf16, gout, f"rank {k}")
+        print(f"gpt2-small rank {k}: all {P} elements ok", flush=True)
     del reps
     _free()
 
 
 def test_gpt2_small_every_partition_in_one_call():
     """All eight ranks' fused steps as one launch (dst = -1, state buffers over
-    the whole padded flat space), sampled per partition against the oracle."""
+    the whole padded flat space), every element of every partition."""
     name = "gpt2-small"
     w = workloads.get(name)
     ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
@@ -109,19 +128,77 @@ def test_gpt2_small_every_partition_in_one_call():
         workloads.device_normal(workloads.seed_for(name, k, master=True), P, w.master_sigma,
                                 DEV, out=master[k * P:(k + 1) * P])
     master[T:] = 0.0
-    idxs = [_sample(P, 20000, 30 + k, [s for s in ref.slices if s.dst == k]) for k in range(R)]
-    th_s = [_gather(master[k * P:(k + 1) * P], idxs[k]) for k in range(R)]
+    th = host_f32(master)
     m, v = torch.zeros(L, device=DEV), torch.zeros(L, device=DEV)
     pbf16 = torch.empty(L, dtype=torch.bfloat16, device=DEV)
     gout = torch.empty(L, device=DEV)
     zr.zr_reduce_scatter_adam(plan, 0, -1, -1, reps, master, m, v, pbf16, gout, **HP)
     for k in range(R):
         sl = slice(k * P, (k + 1) * P)
-        reps_s = [_gather(r_, k * P + idxs[k]) for r_ in reps]
-        _check_fused(reps_s, True, info.divisor, th_s[k], master[sl], m[sl], v[sl],
-                     pbf16[sl], gout[sl], idxs[k])
-        print(f"gpt2-small one call, partition {k}: {idxs[k].size} sampled elements ok")
+        xs = [host_u16(r_[sl]) for r_ in reps]
+        _check_full(xs, True, info.divisor, th[sl], master[sl], m[sl], v[sl], pbf16[sl],
+                    gout[sl], f"one call, partition {k}")
+        print(f"gpt2-small one call, partition {k}: all {P} elements ok", flush=True)
     del reps, master, m, v, pbf16, gout
+    _free()
+
+
+def test_llama3_8b_full_rank_share_in_chunks():
+    """Rank 0's whole Llama-3-8B share (1,003,782,656 elements, 8 fp32
+    replica windows drawn from seeds, three merged slices over buckets 0-2)
+    through one fused call, then every element against the oracle in chunks
+    of 2^26, several chunks checked at once on host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    name = "llama3-8b"
+    w = workloads.get(name)
+    ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    info = ref.groups[0]
+    P, R, k = info.part_numel, info.world, 0
+    # rank 0's slices tile its partition exactly (each element in one slice)
+    mine = sorted((s.part_offset, s.numel) for s in ref.slices if s.dst == k)
+    assert mine[0][0] == 0 and sum(n for _, n in mine) == P
+    assert all(a + n == b for (a, n), (b, _) in zip(mine, mine[1:]))
+    wins = [workloads.device_normal(workloads.seed_for(name, r, 9), P, 2 * w.grad_sigma, DEV)
+            for r in range(R)]
+    master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
+                                     w.master_sigma, DEV)
+    master0 = master.clone()
+    m, v = torch.zeros(P, device=DEV), torch.zeros(P, device=DEV)
+    pbf16 = torch.empty(P, dtype=torch.bfloat16, device=DEV)
+    gout = torch.empty(P, device=DEV)
+    zr.zr_reduce_scatter_adam(plan, 0, -1, k, [(x, 0) for x in wins], master, m, v, pbf16,
+                              gout, **HP)
+    torch.cuda.synchronize()
+    chunk = 1 << 26
+
+    def check(args):
+        lo, xs, th, g, ma, mm, vv, pb = args
+        want_g = rank_order_mean(xs, info.divisor)
+        assert_bits_equal(g, want_g, f"reduced gradient [{lo}, +{g.size})")
+        z = np.zeros_like(th)
+        w_th, w_m, w_v = adam_oracle(want_g, th, z, z, step=1, **HP)
+        assert_within(ma, w_th, what=f"master [{lo}, +{g.size})")
+        assert_within(mm, w_m, what=f"m [{lo}, +{g.size})")
+        assert_within(vv, w_v, atol=0.0, what=f"v [{lo}, +{g.size})")
+        assert np.array_equal(pb, bf16_rne_oracle(ma)), f"bf16 param [{lo}, +{g.size})"
+        return g.size
+
+    done = 0
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        futs = []
+        for lo in range(0, P, chunk):
+            sl = slice(lo, min(P, lo + chunk))
+            futs.append(ex.submit(check, (lo, [host_f32(x[sl]) for x in wins], host_f32(master0[sl]),
+                                          host_f32(gout[sl]), host_f32(master[sl]),
+                                          host_f32(m[sl]), host_f32(v[sl]), host_u16(pbf16[sl]))))
+            if len(futs) >= 6:
+                done += futs.pop(0).result()
+        for f in futs:
+            done += f.result()
+    assert done == P
+    print(f"llama3-8b rank {k}: all {P} elements ok", flush=True)
+    del wins, master, master0, m, v, pbf16, gout
     _free()
 
 

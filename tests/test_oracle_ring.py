@@ -122,3 +122,25 @@ def test_reduce_scatter_then_all_gather_is_all_reduce():
     full = all_gather_oracle([shards[k] for k in range(4)], 2278)
     ar = allreduce_average_oracle(reps, 4, False)
     assert np.array_equal(full.view(np.uint32), ar.view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_step_volume_units_match_simulated_ring_traffic(N):
+    """Each scheme's per-step volume, in units of psi*(N-1)/N, equals what the
+    literal ring simulation sends per card for the collectives the scheme runs
+    (gradient all-reduce = reduce-scatter + all-gather; parameter all-gather)."""
+    C = 5
+    M = N * C
+    unit = Fraction(N - 1, N) * M
+    bufs = [np.ones(M, F) for _ in range(N)]
+    rs_out, rs = ring_reduce_scatter_oracle(bufs)
+    _, ag = ring_all_gather_oracle(rs_out)
+    rs, ag = Fraction(rs[0]), Fraction(ag[0])
+    assert all(Fraction(x) == rs for x in ring_reduce_scatter_oracle(bufs)[1])
+    simulated = {"dp_allreduce": rs + ag,
+                 "zero1_global_allreduce_then_allgather": rs + ag + ag,
+                 "zero_partition_aware": rs + ag,
+                 "grad_sync_reduce_scatter": rs,
+                 "grad_sync_allreduce": rs + ag}
+    for scheme, sent in simulated.items():
+        assert step_volume_units(scheme) * unit == sent, scheme
