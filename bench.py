@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the fused partition reduce-scatter + Adam step on one GPU.
 
-Default workload: GPT-2-small parameter list (124,439,808 elements), 8
-data-parallel replicas of bf16 gradients resident in HBM, reduce_bucket_size
-5e8, fp32 partitions of 1/8.  One step is one rank's whole share of the hot
-path: the fused kernel reads the 8 replica windows of partition k, reduces
-them (pre-divide by 8, rank order), and applies Adam to partition k's fp32
-master / m / v with a bf16 param writeback.  Steps rotate k = 0..7 over eight
-independent state sets, so consecutive launches never reuse cached data.
+Default run (``--workload headline``): the Llama-3-8B-shaped parameter list
+(291 tensors, 8,030,261,248 elements), 8 data-parallel replicas, rank 0's
+share: the fused step reads the 8 fp32 main_grad windows of partition 0
+(1,003,782,656 elements), reduces them (pre-divide by 8, rank order) and
+applies Adam to the partition's fp32 master / m / v with a bf16 param
+writeback -- 58 bytes per partition element, 58.2 GB per step.  The same JSON
+line also carries, each with its own roofline, same-run parity and CPU
+baseline, the GPT-2-small rank shares (8 bf16 replicas, 42 B per element,
+steps rotating over the 8 ranks' state sets) and the MoE step (dense group of
+8 replicas with divisor 4, expert group of 2 with divisor 1, fp32), and a
+same-run copy ceiling (the library's copy kernel moving a 4 GB bucket).
 
-Prints ONE JSON line.  ``value`` is achieved HBM GB/s: algorithmic bytes of a
-step (N*s + 26 bytes per partition element) divided by the measured time per
-step, inputs already resident in HBM.  ``roofline`` prices the dominant
-kernel's average launch duration (HIP events on the launch stream) against
-MI355X's 8 TB/s; ``cpu_baseline`` times the CPU oracle on one rank's
-partition.  Other workloads (``--workload``) are for characterisation.
+Prints ONE JSON line.  ``value`` is achieved HBM GB/s of the headline
+workload: algorithmic bytes of a step divided by the measured time per step,
+inputs already resident in HBM.  ``roofline`` prices the dominant call's
+average duration (HIP events on the launch stream) against MI355X's 8 TB/s;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same work;
+``parity_ok`` says whether sampled outputs of the timed run (and of one more
+call with the reduced gradient written) match the oracle.  Other workloads
+(``--workload``) are for characterisation.
 """
 
 import argparse
@@ -54,7 +60,12 @@ def traffic_for(kernel_key):
     now = kernel_hashes()
     if any(now.get(name) != h for name, h in entry["kernel_sha"].items()):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get("hbm_bytes_per_call")
+
+
+# Calls actually made per label over the whole run (every timer), reported
+# by single-workload runs so counter totals can be divided per call.
+CALLS = {}
 
 
 class Timer:
@@ -70,6 +81,7 @@ class Timer:
         if self.only is not None and label != self.only:
             return
         self.count[label] = self.count.get(label, 0) + 1
+        CALLS[label] = CALLS.get(label, 0) + 1
         fn()
 
 
@@ -86,6 +98,7 @@ class EventTimer(Timer):
             return
         e0 = self.torch.cuda.Event(enable_timing=True)
         e1 = self.torch.cuda.Event(enable_timing=True)
+        CALLS[label] = CALLS.get(label, 0) + 1
         e0.record()
         fn()
         e1.record()
@@ -126,6 +139,99 @@ def timed_region(torch, step, first, steps, only=None):
     return time.perf_counter() - t0, 1e-3 * ev0.elapsed_time(ev1), timer.count
 
 
+# ------------------------------------------------------------ same-run parity
+
+PARITY_SAMPLE = 40000     # random partition elements checked per state set
+
+
+def sample_indices(P, seed, edges=()):
+    """Random partition offsets plus the partition's first and last 2048
+    elements and +-8 elements around each given offset (slice edges)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    idx = set(rng.integers(0, P, size=PARITY_SAMPLE).tolist())
+    idx.update(range(0, min(P, 2048)))
+    idx.update(range(max(0, P - 2048), P))
+    for e in edges:
+        idx.update(range(max(0, e - 8), min(P, e + 8)))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def gather(torch, t, idx):
+    """Values of device tensor t at host indices idx as host numpy (fp32, or
+    the uint16 patterns of bf16)."""
+    import numpy as np
+    g = t[torch.from_numpy(idx).to(t.device)]
+    if g.dtype == torch.bfloat16:
+        return g.cpu().view(torch.int16).numpy().view(np.uint16)
+    return g.cpu().numpy()
+
+
+def track_state(torch, state, idx):
+    """Prepares a state set for the same-run check: the sampled offsets, the
+    initial master there, and a log of the Adam step numbers applied."""
+    state["idx"] = idx
+    state["th0"] = gather(torch, state["master"], idx)
+    state["steps"] = []
+
+
+def check_state(torch, state, xs, is_bf16, D, call):
+    """Checks one state set after the timed run, on its sampled offsets:
+    (1) the oracle replays every logged Adam step from the initial master
+    (m = v = 0) with the oracle's reduced gradient of the replica values
+    ``xs`` (host arrays at the offsets), and the GPU's master, m, v and bf16
+    param must match (Adam within rel 1e-6 / abs 1e-7, v relative only; bf16 =
+    round-to-nearest-even of the GPU's master); (2) one more call,
+    ``call(grad_out, step)``, with the reduced gradient written: bit-exact
+    against the oracle, and its Adam outputs checked the same way."""
+    import numpy as np
+    from oracle.adam import adam_oracle
+    from oracle.bf16 import bf16_rne_oracle
+    from oracle.ipg import widen_bf16
+    from oracle.reduce import rank_order_mean
+    idx = state["idx"]
+    g = rank_order_mean([widen_bf16(x) if is_bf16 else x for x in xs], D)
+    th = state["th0"].copy()
+    m = np.zeros_like(th)
+    v = np.zeros_like(th)
+    for t in state["steps"]:
+        th, m, v = adam_oracle(g, th, m, v, step=t, **HP)
+    worst = {"master": 0.0, "m": 0.0, "v": 0.0}
+
+    def compare(want_th, want_m, want_v):
+        ok = True
+        for name, want, atol in (("master", want_th, 1e-7), ("m", want_m, 1e-7), ("v", want_v, 0.0)):
+            got = gather(torch, state[name], idx).astype(np.float64)
+            w = want.astype(np.float64)
+            err = np.abs(got - w)
+            ok &= bool(np.all(err <= atol + 1e-6 * np.abs(w)))
+            rel = float(np.max(err / np.maximum(np.abs(w), 1e-30)))
+            worst[name] = max(worst[name], rel)
+        pb = gather(torch, state["pbf16"], idx)
+        ok &= bool(np.array_equal(pb, bf16_rne_oracle(gather(torch, state["master"], idx))))
+        return ok
+
+    ok_timed = compare(th, m, v)
+    t = (state["steps"][-1] if state["steps"] else 0) + 1
+    gout = torch.empty_like(state["master"])
+    call(gout, t)
+    torch.cuda.synchronize()
+    got_g = gather(torch, gout, idx)
+    ok_g = bool(np.array_equal(got_g.view(np.uint32), g.view(np.uint32)))
+    th, m, v = adam_oracle(g, th, m, v, step=t, **HP)
+    ok_next = compare(th, m, v)
+    del gout
+    return {"ok": ok_timed and ok_g and ok_next, "elements": int(idx.size),
+            "adam_steps_replayed": len(state["steps"]),
+            "timed_outputs_ok": ok_timed, "reduced_gradient_bit_exact": ok_g,
+            "next_step_ok": ok_next,
+            "max_rel_err": {k: float(f"{x:.3g}") for k, x in worst.items()}}
+
+
+def combine_checks(checks):
+    return {"ok": all(c["ok"] for c in checks.values()), "state_sets": checks}
+
+
 # --------------------------------------------------------------- workloads
 
 def setup_gpt2(torch, zr, workloads, all_ranks=False):
@@ -144,13 +250,34 @@ def setup_gpt2(torch, zr, workloads, all_ranks=False):
                            v=torch.zeros_like(master),
                            pbf16=torch.empty(P, dtype=torch.bfloat16, device="cuda")))
     bytes_per_step = (R * 2 + 26) * P
+    checked = (0, R - 1)                 # state sets the same-run check covers
+    for k in checked:
+        track_state(torch, states[k], sample_indices(P, 100 + k))
 
     def step(i, timer):
         k = i % R
         s = states[k]
-        timer.launch(lambda: zr.zr_reduce_scatter_adam(
-            plan, 0, -1, k, reps, s["master"], s["m"], s["v"], s["pbf16"], None,
-            step=i // R + 1, **HP), "fused")
+        t = i // R + 1
+
+        def call():
+            if "steps" in s:
+                s["steps"].append(t)
+            zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, s["master"], s["m"], s["v"],
+                                      s["pbf16"], None, step=t, **HP)
+        timer.launch(call, "fused")
+
+    def parity():
+        out = {}
+        for k in checked:
+            s = states[k]
+            xs = [gather(torch, r_[k * P:(k + 1) * P], s["idx"]) for r_ in reps]
+            out[f"rank {k}"] = check_state(
+                torch, s, xs, True, D,
+                lambda gout, t: zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, s["master"], s["m"],
+                                                          s["v"], s["pbf16"], gout, step=t, **HP))
+        return combine_checks(out)
+
+    step.parity = parity
 
     cfg = {"workload": name, "params": len(w.numels), "total_elems": T,
            "replicas": R, "grad_dtype": "bf16", "reduce_bucket_size": w.reduce_bucket_size,
@@ -611,11 +738,25 @@ def setup_llama(torch, zr, workloads, ipg=False):
     pbf16 = torch.empty(P, dtype=torch.bfloat16, device="cuda")
     reps = [(x, lo) for x in mgs]
     bytes_per_step = (R * 4 + 26) * P
+    state = dict(master=master, m=m, v=v, pbf16=pbf16)
+    edges = [s_[5] for s_ in zr.zr_plan_slices(plan) if s_[2] == k]     # slice starts
+    track_state(torch, state, sample_indices(P, 200, edges))
 
     def step(i, timer):
-        timer.launch(lambda: zr.zr_reduce_scatter_adam(
-            plan, 0, -1, k, reps, master, m, v, pbf16, None, step=i + 1, **HP), "fused")
+        def call():
+            state["steps"].append(i + 1)
+            zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, master, m, v, pbf16, None,
+                                      step=i + 1, **HP)
+        timer.launch(call, "fused")
 
+    def parity():
+        xs = [gather(torch, x, state["idx"]) for x in mgs]
+        return combine_checks({f"rank {k}": check_state(
+            torch, state, xs, False, D,
+            lambda gout, t: zr.zr_reduce_scatter_adam(plan, 0, -1, k, reps, master, m, v, pbf16,
+                                                      gout, step=t, **HP))})
+
+    step.parity = parity
     cfg.update(grad_dtype="fp32 main_grad", bytes_per_step=bytes_per_step)
     def cpu_leg():
         return cpu_oracle_chunk(torch, mgs, master, P, R, D, 1 << 26)
@@ -643,13 +784,40 @@ def setup_moe(torch, zr, workloads):
         groups.append(dict(R=R, P=P, D=D, reps=reps, states=states, bytes=(R * 4 + 26) * P))
         total_bytes += (R * 4 + 26) * P
 
+    slices = zr.zr_plan_slices(plan)
+    for g, gr in enumerate(groups):
+        for k in (0, gr["R"] - 1):
+            edges = [s_[5] for s_ in slices if s_[1] == g and s_[2] == k]
+            track_state(torch, gr["states"][k], sample_indices(gr["P"], 300 + 10 * g + k, edges))
+
     def step(i, timer):
         for g, gr in enumerate(groups):
             k = i % gr["R"]
             s = gr["states"][k]
-            timer.launch(lambda: zr.zr_reduce_scatter_adam(
-                plan, g, -1, k, gr["reps"], s["master"], s["m"], s["v"], s["pbf16"], None,
-                step=i // gr["R"] + 1, **HP), f"fused_g{g}")
+            t = i // gr["R"] + 1
+
+            def call(g=g, gr=gr, k=k, s=s, t=t):
+                if "steps" in s:
+                    s["steps"].append(t)
+                zr.zr_reduce_scatter_adam(plan, g, -1, k, gr["reps"], s["master"], s["m"],
+                                          s["v"], s["pbf16"], None, step=t, **HP)
+            timer.launch(call, f"fused_g{g}")
+
+    def parity():
+        out = {}
+        for g, gr in enumerate(groups):
+            P_ = gr["P"]
+            for k in (0, gr["R"] - 1):
+                s = gr["states"][k]
+                xs = [gather(torch, r_[k * P_:(k + 1) * P_], s["idx"]) for r_ in gr["reps"]]
+                out[f"group {g} rank {k}"] = check_state(
+                    torch, s, xs, False, gr["D"],
+                    lambda gout, t, g=g, gr=gr, k=k, s=s: zr.zr_reduce_scatter_adam(
+                        plan, g, -1, k, gr["reps"], s["master"], s["m"], s["v"], s["pbf16"],
+                        gout, step=t, **HP))
+        return combine_checks(out)
+
+    step.parity = parity
 
     cfg = {"workload": name, "params": len(w.numels), "groups": w.groups,
            "reduce_bucket_size": w.reduce_bucket_size,
@@ -802,10 +970,13 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
     from concurrent.futures import ThreadPoolExecutor
     from oracle.adam import adam_oracle
     from oracle.bf16 import bf16_rne_oracle
+    from oracle.ipg import widen_bf16
     from oracle.plan import plan_oracle
-    from oracle.reduce import reduce_scatter_oracle
+    from oracle.reduce import rank_order_mean, reduce_scatter_oracle
 
     ref = plan_oracle(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    D = ref.groups[0].divisor
+    assert all(s_.numel == P for s_ in ref.slices)    # one slice per partition
     z = np.zeros(P, np.float32)
     wins = [[r[k * P:(k + 1) * P].cpu().view(torch.int16).numpy().view(np.uint16)
              for r in reps] for k in range(R)]
@@ -823,13 +994,26 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
             one_rank(k)
 
     total, passes = _timed_passes(whole_step)
+    # Parallel leg: every core of the affinity set, each rank's partition
+    # (one slice of the single bucket) cut into pieces, the oracle's per-slice
+    # steps on each piece (numpy's elementwise loops release the interpreter
+    # lock, so the threads run on separate cores).
     avail = len(os.sched_getaffinity(0))
-    threads = max(1, min(R, avail))
+    threads = max(1, avail)
+    cuts = max(1, -(-threads // R))
+    jobs = [(k, P * i // cuts, P * (i + 1) // cuts) for k in range(R) for i in range(cuts)]
+
+    def piece(job):
+        k, a, b = job
+        g = rank_order_mean([widen_bf16(x[a:b]) for x in wins[k]], D)
+        th1, _, _ = adam_oracle(g, masters[k][a:b], z[a:b], z[a:b], step=1, **HP)
+        bf16_rne_oracle(th1)
+
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(lambda k: None, range(threads)))          # start the threads
         t0 = time.perf_counter()
         for _ in range(passes):
-            list(ex.map(one_rank, range(R)))
+            list(ex.map(piece, jobs))
         par = time.perf_counter() - t0
     byts = (R * 2 + 26) * P * R * passes
     elems = P * R * passes
@@ -840,7 +1024,8 @@ def cpu_oracle_fused(torch, workloads, plan, name, w, reps, states, P, R):
                       "numpy single thread",
             "parallel": {"value": round(byts / par / 1e9, 3), "unit": "GB/s", "cores": threads,
                          "elements_per_s": round(elems / par), "seconds": round(par, 3),
-                         "sample": f"the same {passes} passes, one thread per rank"},
+                         "sample": f"the same {passes} passes, each rank's partition in "
+                                   f"{cuts} pieces, {threads} threads"},
             "host_cores_available": avail}
 
 
@@ -869,7 +1054,7 @@ def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
 
     one, passes = _timed_passes(lambda: part(0, n))
     avail = len(os.sched_getaffinity(0))
-    threads = max(1, min(8, avail))
+    threads = max(1, avail)
     cuts = [n * i // threads for i in range(threads + 1)]
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(lambda i: None, range(threads)))
@@ -892,19 +1077,90 @@ def cpu_oracle_chunk(torch, windows, master, P, R, D, chunk):
 
 # --------------------------------------------------------------------- main
 
+def measure(torch, zr, workloads, setup, steps, warmup, workload, cpu=True, check=True):
+    """Times one workload: ``warmup`` untimed steps, then exactly ``steps``
+    steps between HIP events on the launch stream; returns the result dict
+    (value, roofline, launches, same-run parity, CPU baseline)."""
+    step, bytes_per_step, elems_per_step, cfg, launch_bytes, dominant, cpu_leg = \
+        setup(torch, zr, workloads)
+    torch.cuda.synchronize()
+
+    for i in range(warmup):
+        step(i, Timer())
+    torch.cuda.synchronize()
+
+    # The whole step: value and ms_per_step.
+    elapsed, region_s, counts = timed_region(torch, step, warmup, steps)
+    # Average duration of each kind of call: the event-timed region divided by
+    # its calls.  When a step makes more than one kind of call, each kind is
+    # also run back to back on its own (same steps, other calls skipped), so
+    # no event ever sits between two different kernels.
+    per_label_s = {}
+    if len(counts) == 1:
+        (label, n), = counts.items()
+        per_label_s[label] = (n, region_s / n)
+    else:
+        for label in counts:
+            _, r_s, c = timed_region(torch, step, warmup, steps, only=label)
+            per_label_s[label] = (c[label], r_s / c[label])
+    launches = {k: {"count": n, "avg_us": 1e6 * t,
+                    "achieved_GBps": launch_bytes[k] / t / 1e9}
+                for k, (n, t) in per_label_s.items()}
+    # Supplementary: the median of 21 calls of each kind, each bracketed by
+    # its own events (includes the events' own overhead).  Skipped where one
+    # kind of call comes in several sizes (a median of those means nothing).
+    for k in launches:
+        launches[k]["median_us_event_per_launch"] = None if cfg.get("launch_sizes") == \
+            "mixed" else median_launch_us(torch, step, warmup + steps, k)
+    gpu_step_s = region_s / steps
+    wall_step_s = elapsed / steps
+    dom = launches[dominant]
+    roof = {"bound": "hbm", "achieved": round(dom["achieved_GBps"], 1), "peak": PEAK_GBS,
+            "unit": "GB/s", "frac": round(dom["achieved_GBps"] / PEAK_GBS, 4),
+            "traffic": traffic_for(f"{TRAFFIC_SAME_AS.get(workload, workload)}:{dominant}"),
+            "kernel": dominant, "avg_launch_us": round(dom["avg_us"], 2),
+            "median_launch_us_event_per_launch": dom["median_us_event_per_launch"],
+            "algorithmic_bytes_per_launch": launch_bytes[dominant]}
+    out = {"value": round(bytes_per_step / wall_step_s / 1e9, 1), "unit": "GB/s",
+           "steps": steps, "warmup": warmup, "ms_per_step": round(1e3 * wall_step_s, 4),
+           "config": cfg,
+           "pct_of_peak": round(100 * bytes_per_step / wall_step_s / 1e9 / PEAK_GBS, 2),
+           "gpu_region_GBps": round(bytes_per_step / gpu_step_s / 1e9, 1),
+           "elements_per_s": round(elems_per_step / wall_step_s),
+           "launches": launches, "roofline": roof}
+    parity = getattr(step, "parity", None) if check else None
+    if parity is not None:
+        out["parity"] = parity()
+        out["parity_ok"] = out["parity"]["ok"]
+    if cpu_leg is not None and cpu:
+        out["cpu_baseline"] = cpu_leg()
+    del step, cpu_leg, parity
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+HEADLINE = "llama3-8b"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3000)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="gpt2-small",
-                    choices=["gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
                              "llama3-8b-overlap",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
                              "moe-16l-bucketed-graph", "llama3-8b-copy", "gpt2-small-all-ranks",
                              "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the same-run parity check (counter runs: its extra call "
+                         "would be counted with the timed ones)")
     ap.add_argument("--buckets", type=lambda t: [int(float(x)) for x in t.split(",")],
                     default=[int(5e7), int(5e8)],
                     help="reduce_bucket_size values for --workload llama3-8b-overlap")
@@ -936,83 +1192,60 @@ def main():
     if args.workload == "llama3-8b-overlap":
         run_overlap(torch, zr, workloads, args)
         return
-    setup = {"gpt2-small": setup_gpt2, "llama3-8b": setup_llama,
-             "gpt2-small-unfused": setup_gpt2_unfused,
-             "gpt2-small-allgather": setup_gpt2_allgather,
-             "gpt2-small-dp": setup_gpt2_dp,
-             "ring-1gib-allreduce": setup_ring_allreduce,
-             "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
-             "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
-             "moe-16l-bucketed": setup_moe_bucketed,
-             "llama3-8b-copy": setup_llama_copy,
-             "gpt2-small-all-ranks": lambda *a: setup_gpt2(*a, all_ranks=True),
-             "moe-16l-bucketed-graph": lambda *a: setup_moe_bucketed(*a, graph=True),
-             "ring-1gib": setup_ring, "copy": setup_copy}[args.workload]
-    step, bytes_per_step, elems_per_step, cfg, launch_bytes, dominant, cpu_leg = \
-        setup(torch, zr, workloads)
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        step(i, Timer())
-    torch.cuda.synchronize()
-
-    # The whole step: value and ms_per_step.
-    elapsed, region_s, counts = timed_region(torch, step, args.warmup, args.steps)
-    # Average launch duration of each kernel: the event-timed region divided by
-    # its launches.  When a step launches more than one kind of kernel, each
-    # kind is also run back to back on its own (same steps, other launches
-    # skipped), so no event ever sits between two different kernels.
-    per_label_s = {}
-    if len(counts) == 1:
-        (label, n), = counts.items()
-        per_label_s[label] = (n, region_s / n)
+    setups = {"gpt2-small": setup_gpt2, "llama3-8b": setup_llama,
+              "gpt2-small-unfused": setup_gpt2_unfused,
+              "gpt2-small-allgather": setup_gpt2_allgather,
+              "gpt2-small-dp": setup_gpt2_dp,
+              "ring-1gib-allreduce": setup_ring_allreduce,
+              "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
+              "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
+              "moe-16l-bucketed": setup_moe_bucketed,
+              "llama3-8b-copy": setup_llama_copy,
+              "gpt2-small-all-ranks": lambda *a: setup_gpt2(*a, all_ranks=True),
+              "moe-16l-bucketed-graph": lambda *a: setup_moe_bucketed(*a, graph=True),
+              "ring-1gib": setup_ring, "copy": setup_copy}
+    cpu = not args.no_cpu_baseline
+    head_name = HEADLINE if args.workload == "headline" else args.workload
+    check = not args.no_parity
+    head = measure(torch, zr, workloads, setups[head_name], args.steps, args.warmup,
+                   head_name, cpu, check)
+    out = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"),
+           "n_gpus": 1, "steps": head.pop("steps"), "warmup": head.pop("warmup"),
+           "ms_per_step": head.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": head.pop("config")}
+    out.update(head)
+    if args.workload == "headline":
+        # The practical ceiling of a plain stream on this machine, in this run:
+        # the library's own copy kernel moving a 2 GB bucket (5e8 fp32
+        # elements) into a partition, 4 GB of traffic per call.
+        copy = measure(torch, zr, workloads, setup_llama_copy, max(args.steps, 10),
+                       args.warmup, "llama3-8b-copy", False)
+        out["copy_ceiling"] = {"GBps": copy["roofline"]["achieved"],
+                               "frac_of_peak": copy["roofline"]["frac"],
+                               "avg_call_us": copy["roofline"]["avg_launch_us"],
+                               "bytes_per_call": copy["roofline"]["algorithmic_bytes_per_launch"],
+                               "steps": copy["steps"],
+                               "what": "zr_copy_grads_in_partition of a 5e8-element fp32 "
+                                       "bucket into a partition (2 GB read + 2 GB written)"}
+        out["frac_of_copy_ceiling"] = round(out["roofline"]["achieved"] / copy["roofline"]["achieved"], 4)
+        # The other bandwidth workloads, each with its own roofline, parity
+        # and CPU baseline; steps raised so each timed region spans tens of ms.
+        others = {}
+        for name, k_min in (("gpt2-small", 400), ("moe-16l", 20)):
+            steps = max(args.steps, k_min)
+            others[name] = measure(torch, zr, workloads, setups[name], steps,
+                                   max(args.warmup, steps // 10), name, cpu, check)
+        out["other_configs"] = others
+        if check:
+            checks = [out.get("parity_ok")] + [o.get("parity_ok") for o in others.values()]
+            out["parity_ok"] = all(c is True for c in checks)
     else:
-        for label in counts:
-            _, r_s, c = timed_region(torch, step, args.warmup, args.steps, only=label)
-            per_label_s[label] = (c[label], r_s / c[label])
-    launches = {k: {"count": n, "avg_us": 1e6 * t,
-                    "achieved_GBps": launch_bytes[k] / t / 1e9}
-                for k, (n, t) in per_label_s.items()}
-    # Supplementary: the median of 21 launches of each kind, each bracketed by
-    # its own events (includes the events' own overhead).  Skipped where one
-    # kind of launch comes in several sizes (a median of those means nothing).
-    for k in launches:
-        launches[k]["median_us_event_per_launch"] = None if cfg.get("launch_sizes") == \
-            "mixed" else median_launch_us(torch, step, args.warmup + args.steps, k)
-    gpu_step_s = region_s / args.steps
-    wall_step_s = elapsed / args.steps
-    dom = launches[dominant]
-    roof = {"bound": "hbm", "achieved": round(dom["achieved_GBps"], 1), "peak": PEAK_GBS,
-            "unit": "GB/s", "frac": round(dom["achieved_GBps"] / PEAK_GBS, 4),
-            "traffic": traffic_for(f"{TRAFFIC_SAME_AS.get(args.workload, args.workload)}:{dominant}"),
-            "kernel": dominant, "avg_launch_us": round(dom["avg_us"], 2),
-            "median_launch_us_event_per_launch": dom["median_us_event_per_launch"],
-            "algorithmic_bytes_per_launch": launch_bytes[dominant]}
-
-    out = {
-        "metric": METRIC,
-        "value": round(bytes_per_step / wall_step_s / 1e9, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(1e3 * wall_step_s, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": cfg,
-        "pct_of_peak": round(100 * bytes_per_step / wall_step_s / 1e9 / PEAK_GBS, 2),
-        "gpu_region_GBps": round(bytes_per_step / gpu_step_s / 1e9, 1),
-        "elements_per_s": round(elems_per_step / wall_step_s),
-        "launches": launches,
-        "roofline": roof,
-        "device": torch.cuda.get_device_name(0),
-    }
-    if cpu_leg is not None and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_leg()
+        out["calls_made"] = dict(CALLS)
+    out["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(out), flush=True)
+    if out.get("parity_ok") is False:
+        sys.exit(1)
 
 
 if __name__ == "__main__":
