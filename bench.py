@@ -835,14 +835,16 @@ def setup_moe(torch, zr, workloads):
         {f"fused_g{g}": gr["bytes"] for g, gr in enumerate(groups)}, "fused_g1", cpu_leg
 
 
-def setup_moe_bucketed(torch, zr, workloads, graph=False):
-    """The MoE step through the bucketed path of the pages' IPG design: for
-    rank 0 of each group, one reduce-scatter call per (bucket, group) that
-    has slices for that rank (269 buckets of 5e6 elements, both groups
-    interleaved), into the rank's fp32 gradient partition, then Adam over
-    each partition.  With ``graph`` the whole step is captured once in a HIP
-    graph (torch.cuda.CUDAGraph) and each step is one replay: the step is
-    launch-bound (hundreds of small launches), which is what graphs remove."""
+def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
+    """The MoE step through the bucketed path of the pages' IPG design, for
+    rank 0 of each group: reduce-scatter calls into the rank's fp32 gradient
+    partitions (269 buckets of 5e6 elements, both groups interleaved), then
+    Adam over each partition.  By default each call takes every bucket
+    completed since the previous one (zr_reduce_scatter_local_range), a call
+    per group after each layer's 17 parameters, taken in list order as the
+    ready order; with ``per_bucket`` one call per (bucket, group) holding
+    slices for the rank.  With ``graph`` the whole step is captured once in a
+    HIP graph (torch.cuda.CUDAGraph) and each step is one replay."""
     name = "moe-16l"
     w = workloads.get(name)
     plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
@@ -861,32 +863,49 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False):
                            v=torch.zeros_like(master),
                            pbf16=torch.empty(P, dtype=torch.bfloat16, device="cuda")))
         total_bytes += (R * 4 + 4 + 30) * P
-    # (bucket, group) selections holding slices for rank k, plus the last
-    # bucket of every group (it also writes the group's padding).
-    pairs = []
-    for b in range(nb):
-        sl = zr.zr_plan_slices(plan, b)
-        for g in range(len(groups)):
-            if b == nb - 1 or any(s[1] == g and s[2] == k for s in sl):
-                pairs.append((b, g))
+    if per_bucket:
+        # (bucket, group) selections holding slices for rank k, plus the last
+        # bucket of every group (it also writes the group's padding).
+        calls = []
+        for b in range(nb):
+            sl = zr.zr_plan_slices(plan, b)
+            for g in range(len(groups)):
+                if b == nb - 1 or any(s[1] == g and s[2] == k for s in sl):
+                    calls.append((g, b, 1))
+    else:
+        # Ranges: after each layer, the buckets completed since the last call.
+        per_layer = 17
+        B = w.reduce_bucket_size
+        calls, done, pos = [], 0, 0
+        for p, ne in enumerate(w.numels):
+            pos += ne
+            if (p + 1) % per_layer == 0 or p + 1 == len(w.numels):
+                full = nb if p + 1 == len(w.numels) else pos // B
+                if full > done:
+                    calls += [(g, done, full - done) for g in range(len(groups))]
+                    done = full
+        assert done == nb
 
     def eager(t, timer):
-        for b, g in pairs:
+        for g, b, n in calls:
             gr = groups[g]
-            timer.launch(lambda: zr.zr_reduce_scatter_local(plan, g, b, k, gr["reps"],
-                                                            [gr["grad"]]), "reduce")
+            timer.launch(lambda: zr.zr_reduce_scatter_local_range(plan, g, b, n, k, gr["reps"],
+                                                                  [gr["grad"]]), "reduce")
         for gr in groups:
             timer.launch(lambda: zr.zr_adam_partition(gr["grad"], gr["master"], gr["m"],
                                                       gr["v"], gr["pbf16"], step=t, **HP),
                          "adam")
 
-    # Per-launch bytes of each kind, averaged over the step's launches of it.
-    launch_bytes = {"reduce": round(sum((gr["R"] * 4 + 4) * gr["P"] for gr in groups) / len(pairs)),
+    # Per-call bytes of each kind, averaged over the step's calls of it.
+    launch_bytes = {"reduce": round(sum((gr["R"] * 4 + 4) * gr["P"] for gr in groups) / len(calls)),
                     "adam": round(sum(30 * gr["P"] for gr in groups) / len(groups))}
-    cfg = {"workload": name + ("-bucketed-graph" if graph else "-bucketed"),
+    cfg = {"workload": name + ("-per-bucket" if per_bucket else "-bucketed") +
+           ("-graph" if graph else ""),
            "params": len(w.numels), "groups": w.groups, "rank": k,
            "reduce_bucket_size": w.reduce_bucket_size, "buckets": nb,
-           "reduce_launches_per_step": len(pairs), "adam_launches_per_step": len(groups),
+           "trigger": "one call per (bucket, group) with slices for the rank" if per_bucket
+           else "after each layer, one call per group for the buckets completed since the last",
+           "reduce_calls_per_step": len(calls), "adam_calls_per_step": len(groups),
            "partition_elems": [gr["P"] for gr in groups], "grad_dtype": "fp32",
            "bytes_per_step": total_bytes, "launch_sizes": "mixed"}
     if not graph:
@@ -1155,7 +1174,8 @@ def main():
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
                              "llama3-8b-overlap",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
-                             "moe-16l-bucketed-graph", "llama3-8b-copy", "gpt2-small-all-ranks",
+                             "moe-16l-per-bucket", "moe-16l-per-bucket-graph",
+                             "llama3-8b-copy", "gpt2-small-all-ranks",
                              "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true",
@@ -1202,7 +1222,9 @@ def main():
               "moe-16l-bucketed": setup_moe_bucketed,
               "llama3-8b-copy": setup_llama_copy,
               "gpt2-small-all-ranks": lambda *a: setup_gpt2(*a, all_ranks=True),
-              "moe-16l-bucketed-graph": lambda *a: setup_moe_bucketed(*a, graph=True),
+              "moe-16l-per-bucket": lambda *a: setup_moe_bucketed(*a, per_bucket=True),
+              "moe-16l-per-bucket-graph": lambda *a: setup_moe_bucketed(*a, graph=True,
+                                                                          per_bucket=True),
               "ring-1gib": setup_ring, "copy": setup_copy}
     cpu = not args.no_cpu_baseline
     head_name = HEADLINE if args.workload == "headline" else args.workload

@@ -229,6 +229,24 @@ zr_status zr_reduce_scatter_local(const zr_plan* plan, int32_t group,
                                   const zr_replica* reps, zr_dtype grad_dtype,
                                   float* const* part_out, hipStream_t stream);
 
+/* zr_reduce_scatter_local_range -- zr_reduce_scatter_local over the buckets
+ * [bucket_first, bucket_first + bucket_count) in one call: every bucket
+ * completed since the last call reduced together ([ZeRO-RS blog §四]: each
+ * IPG bucket is reduced once it is full; [Megatron DP]
+ * "梯度缓冲区+分桶+overlap": a bucket's gradient sync starts once all its
+ * grads are ready).  Results are bit-identical to one zr_reduce_scatter_local
+ * call per bucket; the range is carried by one launch table (built on its
+ * first use, like any selection's) and as few launches as its traffic allows,
+ * instead of one launch per bucket.  bucket_count == 0 enqueues nothing;
+ * ZR_ERR_INVALID when bucket_first < 0, bucket_count < 0 or the range runs
+ * past the last bucket.  Padding is written when the range covers the last
+ * bucket. */
+zr_status zr_reduce_scatter_local_range(const zr_plan* plan, int32_t group,
+                                        int64_t bucket_first, int64_t bucket_count,
+                                        int32_t dst, const zr_replica* reps,
+                                        zr_dtype grad_dtype, float* const* part_out,
+                                        hipStream_t stream);
+
 /* zr_copy_grads_in_partition -- the standalone copy of already reduced slices
  * into the local contiguous partition buffer ([ZeRO-RS blog §三.3]):
  *   part_out[part_offset + j] = bucket_layout_src[bucket_offset + j]
@@ -268,6 +286,20 @@ zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
                                  const zr_adam* h, float* master, float* m,
                                  float* v, uint16_t* param_bf16,
                                  float* grad_out, hipStream_t stream);
+
+/* zr_reduce_scatter_adam_range -- zr_reduce_scatter_adam over the buckets
+ * [bucket_first, bucket_first + bucket_count), the fused counterpart of
+ * zr_reduce_scatter_local_range (same citations and range rules).
+ * Bit-identical to one zr_reduce_scatter_adam call per bucket: Adam updates
+ * only the elements of the selected slices (plus the padding when the range
+ * covers the last bucket). */
+zr_status zr_reduce_scatter_adam_range(const zr_plan* plan, int32_t group,
+                                       int64_t bucket_first, int64_t bucket_count,
+                                       int32_t dst, const zr_replica* reps,
+                                       zr_dtype grad_dtype, const zr_adam* h,
+                                       float* master, float* m, float* v,
+                                       uint16_t* param_bf16, float* grad_out,
+                                       hipStream_t stream);
 
 /* zr_reduce_scatter_adam_capped -- zr_reduce_scatter_adam on a launch of at
  * most max_workgroups workgroups (>= 1; ZR_ERR_INVALID otherwise), each

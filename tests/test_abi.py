@@ -336,3 +336,36 @@ def test_kernel_fingerprints_cover_the_measured_kernels():
     for key, entry in traffic.items():
         for name in entry["kernel_sha"]:
             assert name in hashes, f"{key}: kernel {name!r} is not in the built library"
+
+
+def test_range_calls_check_their_range():
+    """A bucket range must lie inside the plan; an empty range enqueues
+    nothing (and needs no GPU)."""
+    plan = _tiny_plan()                      # 3 buckets
+    reps = [_FakeTensor(0x1000 * (i + 1), 2280) for i in range(4)]
+    buf = _FakeTensor(0x100000, 570)
+    for first, count in ((-1, 1), (0, -1), (2, 2), (4, 0)):
+        with pytest.raises(zr.ZrError, match="bucket") as ei:
+            zr.zr_reduce_scatter_local_range(plan, 0, first, count, 0, reps, [buf], stream=0)
+        assert ei.value.status == zr.ZR_ERR_INVALID
+        with pytest.raises(zr.ZrError, match="bucket"):
+            zr.zr_reduce_scatter_adam_range(plan, 0, first, count, 0, reps, buf, buf, buf,
+                                            stream=0)
+    for first in (0, 3):
+        zr.zr_reduce_scatter_local_range(plan, 0, first, 0, 0, reps, [buf], stream=0)
+        zr.zr_reduce_scatter_adam_range(plan, 0, first, 0, 1, reps, buf, buf, buf, stream=0)
+    call = zr.prepare_reduce_scatter_adam(plan, 0, 2, reps, buf, buf, buf)
+    call(1, 1, stream=0, count=0)
+    with pytest.raises(zr.ZrError, match="bucket"):
+        call(1, 1, stream=0, count=3)
+
+
+def test_binding_handles_a_group_without_params():
+    """A group that no param belongs to has no elements (P_g = 0); list
+    lengths are still checked against its world size."""
+    plan = zr.zr_plan_buckets([10, 20], [0, 0], [(2, 1), (4, 1)], 16)
+    assert zr.zr_plan_group_info(plan, 1)[:3] == (0, 0, 0)
+    reps = [_FakeTensor(0x1000 * (i + 1), 30) for i in range(4)]
+    zr.zr_reduce_scatter_local(plan, 1, -1, 0, reps, [_FakeTensor(0x100000, 0)], stream=0)
+    with pytest.raises(zr.ZrError, match="reps has 3 entries; the call needs 4"):
+        zr.zr_reduce_scatter_local(plan, 1, -1, 0, reps[:3], [_FakeTensor(0x100000, 0)], stream=0)

@@ -57,7 +57,7 @@
 #include <string>
 #include <type_traits>
 #include <tuple>
-#include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "zr_internal.h"
@@ -1134,8 +1134,9 @@ struct DevTable {
   int device = 0;
 };
 enum TableKind { kReduceTable = 0, kCopyTable = 1 };
-using HostKey = std::tuple<int, int32_t, int64_t, int32_t>;      // kind, group, bucket, dst
-using DevKey = std::tuple<int, int, int32_t, int64_t, int32_t>;  // device + HostKey
+// kind, group, first bucket, end bucket (exclusive), dst
+using HostKey = std::tuple<int, int32_t, int64_t, int64_t, int32_t>;
+using DevKey = std::tuple<int, int, int32_t, int64_t, int64_t, int32_t>;  // device + HostKey
 
 struct DevCache {
   std::mutex mu;
@@ -1211,15 +1212,15 @@ int64_t launches_for(int64_t total, int64_t tile_bytes) {
 // Tiles [first, end) of launch i of n over `total` tiles.
 int64_t launch_first(int64_t total, int64_t n, int64_t i) { return total * i / n; }
 
-// Segments of `group`, `bucket` (-1 all), `dst` (-1 all) in bucket order, plus
-// the padding of the selected partitions when the call covers the last bucket
+// Segments of `group` in buckets [first, last), `dst` (-1 all) in bucket order,
+// plus the padding of the selected partitions when the range covers the last
+// bucket
 // (reduce tables only); each gets its tile offset.
 std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
-                                int64_t bucket, int32_t dst) {
+                                int64_t first, int64_t last, int32_t dst) {
   std::vector<Seg> out;
-  const int64_t a = bucket < 0 ? 0 : plan->bucket_first[bucket];
-  const int64_t b = bucket < 0 ? static_cast<int64_t>(plan->slices.size())
-                               : plan->bucket_first[bucket + 1];
+  const int64_t a = plan->bucket_first[first];
+  const int64_t b = plan->bucket_first[last];
   for (int64_t i = a; i < b; ++i) {
     const zr_slice& s = plan->slices[i];
     if (s.group != group || (dst >= 0 && s.dst != dst)) continue;
@@ -1231,7 +1232,7 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
     g.pad = 0;
     out.push_back(g);
   }
-  if (kind == kReduceTable && (bucket < 0 || bucket == plan->num_buckets - 1)) {
+  if (kind == kReduceTable && first < last && last == plan->num_buckets) {
     const zr::GroupInfo& gi = plan->groups[group];
     for (int32_t k = 0; k < gi.world; ++k) {
       if (dst >= 0 && k != dst) continue;
@@ -1259,16 +1260,16 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
 }
 
 // Host segment list for a call (no HIP call is made).
-zr_status get_host_table(const zr_plan* plan, int kind, int32_t group, int64_t bucket,
-                         int32_t dst, const std::vector<Seg>** out) {
+zr_status get_host_table(const zr_plan* plan, int kind, int32_t group, int64_t first,
+                         int64_t last, int32_t dst, const std::vector<Seg>** out) {
   DevCache* c = cache_of(plan);
   std::lock_guard<std::mutex> lk(c->mu);
-  const HostKey key{kind, group, bucket, dst};
+  const HostKey key{kind, group, first, last, dst};
   auto it = c->host.find(key);
   if (it == c->host.end()) {
     HostTable t;
     try {
-      t.segs = build_segments(plan, kind, group, bucket, dst);
+      t.segs = build_segments(plan, kind, group, first, last, dst);
     } catch (const std::bad_alloc&) {
       return fail(ZR_ERR_OOM, "out of host memory building a launch table");
     }
@@ -1279,12 +1280,12 @@ zr_status get_host_table(const zr_plan* plan, int kind, int32_t group, int64_t b
 }
 
 // Device copy of the same list on `device` (synchronous upload on first use).
-zr_status get_dev_table(const zr_plan* plan, int kind, int32_t group, int64_t bucket,
-                        int32_t dst, int device, const std::vector<Seg>& host,
+zr_status get_dev_table(const zr_plan* plan, int kind, int32_t group, int64_t first,
+                        int64_t last, int32_t dst, int device, const std::vector<Seg>& host,
                         const Seg** out) {
   DevCache* c = cache_of(plan);
   std::lock_guard<std::mutex> lk(c->mu);
-  const DevKey key{device, kind, group, bucket, dst};
+  const DevKey key{device, kind, group, first, last, dst};
   auto it = c->dev.find(key);
   if (it != c->dev.end()) {
     *out = it->second.dev;
@@ -1414,7 +1415,8 @@ zr_status stage_segments(const Seg* segs, int64_t n, Seg* table, hipStream_t str
 // Shared validation + launch of the reduce kernel in either mode; max_wgs > 0
 // caps the grid (0: one workgroup per tile).  noalloc: the segment table is
 // staged in `scratch` instead of the plan's device table.
-zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t dst,
+zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t last,
+                     int32_t dst,
                      const zr_replica* reps, zr_dtype dt, float* const* part_out,
                      const zr_adam* h, float* master, float* m, float* v,
                      uint16_t* pbf16, float* gout, bool fused, int64_t max_wgs,
@@ -1423,7 +1425,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
   if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
   if (group < 0 || group >= static_cast<int32_t>(plan->groups.size()))
     return fail(ZR_ERR_INVALID, "group index out of range");
-  if (bucket < -1 || bucket >= plan->num_buckets)
+  if (first < 0 || last > plan->num_buckets || first > last)
     return fail(ZR_ERR_INVALID, "bucket index out of range");
   const zr::GroupInfo& gi = plan->groups[group];
   if (dst < -1 || dst >= gi.world) return fail(ZR_ERR_INVALID, "dst out of range");
@@ -1465,7 +1467,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
     }
   }
   const std::vector<Seg>* hs = nullptr;
-  zr_status st = get_host_table(plan, kReduceTable, group, bucket, dst, &hs);
+  zr_status st = get_host_table(plan, kReduceTable, group, first, last, dst, &hs);
   if (st != ZR_OK) return st;
   const int nseg = static_cast<int>(hs->size()) - 1;
   // Every replica window must cover every slice this call reads.
@@ -1543,7 +1545,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
     if (st != ZR_OK) return st;
     a.segs = table;
   } else if (!argsegs) {
-    st = get_dev_table(plan, kReduceTable, group, bucket, dst, device, *hs, &a.segs);
+    st = get_dev_table(plan, kReduceTable, group, first, last, dst, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
   RedArgsS as;
@@ -1573,13 +1575,46 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t bucket, int32_t
 
 // =============================================================== C ABI ===
 
+namespace {
+// A call's bucket argument (-1 = every bucket) as a range [first, last);
+// out-of-range values give an empty-checked range that run_reduce rejects.
+std::pair<int64_t, int64_t> bucket_range(const zr_plan* plan, int64_t bucket) {
+  if (!plan) return {0, 0};
+  if (bucket == -1) return {0, plan->num_buckets};
+  if (bucket < -1 || bucket >= plan->num_buckets) return {1, 0};   // invalid
+  return {bucket, bucket + 1};
+}
+// [first, first + count) as a range, or an invalid one.
+std::pair<int64_t, int64_t> count_range(const zr_plan* plan, int64_t first, int64_t count) {
+  if (!plan || first < 0 || count < 0 || first > plan->num_buckets ||
+      count > plan->num_buckets - first)
+    return {1, 0};   // invalid
+  return {first, first + count};
+}
+}  // namespace
+
 extern "C" zr_status zr_reduce_scatter_local(const zr_plan* plan, int32_t group,
                                              int64_t bucket, int32_t dst,
                                              const zr_replica* reps, zr_dtype grad_dtype,
                                              float* const* part_out, hipStream_t stream) {
   try {
-    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, part_out, nullptr,
-                      nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, stream);
+    const auto r = bucket_range(plan, bucket);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, part_out,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, stream);
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
+
+extern "C" zr_status zr_reduce_scatter_local_range(const zr_plan* plan, int32_t group,
+                                                   int64_t bucket_first, int64_t bucket_count,
+                                                   int32_t dst, const zr_replica* reps,
+                                                   zr_dtype grad_dtype, float* const* part_out,
+                                                   hipStream_t stream) {
+  try {
+    const auto r = count_range(plan, bucket_first, bucket_count);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, part_out,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, stream);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1592,8 +1627,25 @@ extern "C" zr_status zr_reduce_scatter_adam(const zr_plan* plan, int32_t group,
                                             float* v, uint16_t* param_bf16,
                                             float* grad_out, hipStream_t stream) {
   try {
-    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
-                      v, param_bf16, grad_out, true, 0, stream);
+    const auto r = bucket_range(plan, bucket);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, nullptr, h,
+                      master, m, v, param_bf16, grad_out, true, 0, stream);
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
+
+extern "C" zr_status zr_reduce_scatter_adam_range(const zr_plan* plan, int32_t group,
+                                                  int64_t bucket_first, int64_t bucket_count,
+                                                  int32_t dst, const zr_replica* reps,
+                                                  zr_dtype grad_dtype, const zr_adam* h,
+                                                  float* master, float* m, float* v,
+                                                  uint16_t* param_bf16, float* grad_out,
+                                                  hipStream_t stream) {
+  try {
+    const auto r = count_range(plan, bucket_first, bucket_count);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, nullptr, h,
+                      master, m, v, param_bf16, grad_out, true, 0, stream);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1612,8 +1664,9 @@ extern "C" zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t 
       zr::clear_error();
       return fail(ZR_ERR_INVALID, "max_workgroups must be >= 1");
     }
-    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
-                      v, param_bf16, grad_out, true, max_workgroups, stream);
+    const auto r = bucket_range(plan, bucket);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, nullptr, h,
+                      master, m, v, param_bf16, grad_out, true, max_workgroups, stream);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1627,8 +1680,9 @@ extern "C" zr_status zr_reduce_scatter_adam_noalloc(const zr_plan* plan, int32_t
                                                     uint16_t* param_bf16, float* grad_out,
                                                     hipStream_t stream) {
   try {
-    return run_reduce(plan, group, bucket, dst, reps, grad_dtype, nullptr, h, master, m,
-                      v, param_bf16, grad_out, true, 0, stream, true);
+    const auto r = bucket_range(plan, bucket);
+    return run_reduce(plan, group, r.first, r.second, dst, reps, grad_dtype, nullptr, h,
+                      master, m, v, param_bf16, grad_out, true, 0, stream, true);
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
@@ -1783,7 +1837,7 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
         !elem_aligned(part_out, 4))
       return fail(ZR_ERR_INVALID, "buffers are null or not element-aligned");
     const std::vector<Seg>* hs = nullptr;
-    zr_status st = get_host_table(plan, kCopyTable, group, bucket, dst, &hs);
+    zr_status st = get_host_table(plan, kCopyTable, group, bucket, bucket + 1, dst, &hs);
     if (st != ZR_OK) return st;
     const int nseg = static_cast<int>(hs->size()) - 1;
     if (nseg == 0) return ZR_OK;
@@ -1791,7 +1845,7 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
     st = device_info(&device, &cus);
     if (st != ZR_OK) return st;
     CopyArgs a{};
-    st = get_dev_table(plan, kCopyTable, group, bucket, dst, device, *hs, &a.segs);
+    st = get_dev_table(plan, kCopyTable, group, bucket, bucket + 1, dst, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
     a.src = bucket_layout_src;
     a.dst = part_out;

@@ -98,6 +98,11 @@ _sigs = {
                                   c_i64, c_i64, c_vp]),
     "zr_reduce_scatter_local": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
                                         c_i32, _P(c_vp), c_vp]),
+    "zr_reduce_scatter_local_range": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32,
+                                              _P(zr_replica), c_i32, _P(c_vp), c_vp]),
+    "zr_reduce_scatter_adam_range": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32,
+                                             _P(zr_replica), c_i32, _P(zr_adam), c_vp, c_vp,
+                                             c_vp, c_vp, c_vp, c_vp]),
     "zr_copy_grads_in_partition": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_vp,
                                            c_vp]),
     "zr_adam_partition": (c_i32, [_P(zr_adam), c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -223,13 +228,12 @@ def _padded_numel(plan, group):
 
 
 def _world(plan, group):
-    """R_g of the plan's group (L_g / P_g), queried once per plan and group."""
-    key = ("world", group)
-    R = plan.part_numel.get(key)
-    if R is None:
-        _, L, P, _ = zr_plan_group_info(plan, group)
-        R = plan.part_numel[key] = L // P
-    return R
+    """R_g of the plan's group, as given to zr_plan_buckets (an out-of-range
+    group is the C call's error: the group query raises it)."""
+    g = _i32(group, "group")
+    if not 0 <= g < len(plan.worlds):
+        zr_plan_group_info(plan, g)
+    return plan.worlds[g]
 
 
 def _expect_len(seq, n, name):
@@ -265,10 +269,11 @@ def _adam(lr, beta1, beta2, eps, step):
 class Plan:
     """Owns a zr_plan handle (freed with zr_plan_free)."""
 
-    def __init__(self, handle, numels=()):
+    def __init__(self, handle, numels=(), worlds=()):
         self._h = handle
         self.part_numel = {}      # group -> P_g (the plan is immutable)
         self.numels = tuple(int(n) for n in numels)   # param sizes, list order
+        self.worlds = tuple(int(w) for w in worlds)   # R_g per group
 
     @property
     def handle(self):
@@ -304,7 +309,7 @@ def zr_plan_buckets(numels, param_groups, groups, reduce_bucket_size,
                                 _i32(partition_gradients, "partition_gradients"),
                                 _i64(align, "align"),
                                 ctypes.byref(out)))
-    return Plan(out.value, numels)
+    return Plan(out.value, numels, [w for w, _ in groups])
 
 
 def zr_plan_free(plan):
@@ -427,6 +432,43 @@ def zr_reduce_scatter_local(plan, group, bucket, dst, reps, part_out,
                                         _stream(stream)))
 
 
+def zr_reduce_scatter_local_range(plan, group, bucket_first, bucket_count, dst, reps,
+                                  part_out, stream=None):
+    """zr_reduce_scatter_local over buckets [bucket_first, bucket_first +
+    bucket_count) in one call."""
+    arr, dt = _replicas(reps, plan, group)
+    P = _part_numel(plan, group)
+    R = _world(plan, group)
+    if -1 <= _i32(dst, "dst") < R:        # an out-of-range dst is the C call's error
+        _expect_len(part_out, R if int(dst) == -1 else 1, "part_out")
+    outs = (c_vp * max(len(part_out), 1))(
+        *[_buf(t, f"part_out[{i}]", ZR_FP32, P).value if t is not None else None
+          for i, t in enumerate(part_out)])
+    _check(_lib.zr_reduce_scatter_local_range(plan.handle, _i32(group, "group"),
+                                              _i64(bucket_first, "bucket_first"),
+                                              _i64(bucket_count, "bucket_count"),
+                                              _i32(dst, "dst"), arr, dt, outs, _stream(stream)))
+
+
+def zr_reduce_scatter_adam_range(plan, group, bucket_first, bucket_count, dst, reps,
+                                 master, m, v, param_bf16=None, grad_out=None, lr=1e-3,
+                                 beta1=0.9, beta2=0.999, eps=1e-8, step=1, stream=None):
+    """zr_reduce_scatter_adam over buckets [bucket_first, bucket_first +
+    bucket_count) in one call."""
+    arr, dt = _replicas(reps, plan, group)
+    h = _adam(lr, beta1, beta2, eps, step)
+    P = _part_numel(plan, group) if int(dst) >= 0 else _padded_numel(plan, group)
+    _check(_lib.zr_reduce_scatter_adam_range(plan.handle, _i32(group, "group"),
+                                             _i64(bucket_first, "bucket_first"),
+                                             _i64(bucket_count, "bucket_count"),
+                                             _i32(dst, "dst"), arr, dt, ctypes.byref(h),
+                                             _buf(master, "master", ZR_FP32, P),
+                                             _buf(m, "m", ZR_FP32, P), _buf(v, "v", ZR_FP32, P),
+                                             _buf(param_bf16, "param_bf16", ZR_BF16, P),
+                                             _buf(grad_out, "grad_out", ZR_FP32, P),
+                                             _stream(stream)))
+
+
 def zr_copy_grads_in_partition(plan, group, bucket, dst, bucket_layout_src,
                                part_out, stream=None):
     need = 0
@@ -535,9 +577,18 @@ class PreparedReduceScatterAdam:
             raise ZrError(ZR_ERR_INVALID, "max_workgroups must be >= 0 (0: uncapped)")
         self._handle = plan.handle
 
-    def __call__(self, bucket=-1, step=1, stream=None):
+    def __call__(self, bucket=-1, step=1, stream=None, count=None):
+        """``count`` given: the buckets [bucket, bucket + count) in one call
+        (zr_reduce_scatter_adam_range; not with a workgroup cap)."""
         self._h.step = _i64(step, "step")
         b = _i64(bucket, "bucket")
+        if count is not None:
+            if self._cap:
+                raise ZrError(ZR_ERR_INVALID, "a bucket range cannot be capped")
+            _check(_lib.zr_reduce_scatter_adam_range(
+                self._handle, self._group, b, _i64(count, "count"), self._dst, self._arr,
+                self._dt, ctypes.byref(self._h), *self._bufs, _stream(stream)))
+            return
         if self._cap:
             _check(_lib.zr_reduce_scatter_adam_capped(
                 self._handle, self._group, b, self._dst, self._arr, self._dt,
