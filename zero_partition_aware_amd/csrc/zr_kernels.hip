@@ -94,6 +94,13 @@ namespace {
 #ifndef ZR_NT_STORES
 #define ZR_NT_STORES 1
 #endif
+// Launch of kernel __VA_ARGS__ over `grid` workgroups of `block` lanes on
+// `stream` with the argument block `args` (a CPU build of this file for
+// bounds checking substitutes its own).
+#ifndef ZR_KERNEL_LAUNCH
+#define ZR_KERNEL_LAUNCH(grid, block, stream, args, ...) \
+  __VA_ARGS__<<<(grid), (block), 0, (stream)>>>(args)
+#endif
 constexpr int kThreads = ZR_THREADS;
 constexpr int64_t kTileElems = ZR_TILE_ELEMS;
 constexpr int VE = 4;  // elements per lane slot
@@ -145,16 +152,16 @@ constexpr int64_t kRingAgTileElems = int64_t(kRingAgSlots) * kThreads * VE;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// The same vectors with only dword (4-byte) alignment assumed, for the
-// kernels' dword-aligned variants (reduce, IPG, Adam, copy, all-gather).  A
-// global load or store of two or four dwords needs a dword-aligned address
-// only (the hardware ignores the two low address bits of dword-or-larger
-// accesses).  Each variant is a separate instantiation that the host launches
-// only when some segment has no phase at which every stream is slot-aligned,
-// so the common instantiations carry none of its code.
-typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
-typedef unsigned int u32x2d __attribute__((ext_vector_type(2), aligned(4)));
-typedef float f32x4d __attribute__((ext_vector_type(4), aligned(4)));
+// Alignment a vector access may assume.  The kernels' dword-aligned variants
+// (reduce, IPG, Adam, copy, ring steps, all-gather) access two- and
+// four-dword vectors at merely dword-aligned addresses, which global loads
+// and stores of this part accept.  Each variant is a separate instantiation
+// that the host launches only when some segment has no phase at which every
+// stream is slot-aligned, so the common instantiations carry none of its
+// code.  The alignment travels as a template value (kDW), not as an aligned()
+// typedef: template arguments are canonical types, so a typedef's reduced
+// alignment would be lost inside the access helpers.
+constexpr int kDW = 4;
 
 // ------------------------------------------------------------ device helpers
 
@@ -162,7 +169,9 @@ typedef float f32x4d __attribute__((ext_vector_type(4), aligned(4)));
 // through global-address-space pointers lets the compiler use global_load /
 // global_store with a uniform 64-bit base and a 32-bit lane offset instead of
 // flat instructions with a 64-bit address per lane.
+#ifndef ZR_GLOBAL
 #define ZR_GLOBAL __attribute__((address_space(1)))
+#endif
 template <typename T>
 __device__ __forceinline__ const ZR_GLOBAL T* gptr(const void* p) {
   return (const ZR_GLOBAL T*)(p);
@@ -172,60 +181,66 @@ __device__ __forceinline__ ZR_GLOBAL T* gptr(void* p) {
   return (ZR_GLOBAL T*)(p);
 }
 
-template <typename T>
+// A access (load or store) of T that may assume A-byte alignment (A = 0: T's
+// natural alignment).
+template <typename T, int A = 0>
 __device__ __forceinline__ T ld_global(const ZR_GLOBAL T* p) {
+  typedef T __attribute__((aligned(A ? A : alignof(T)))) TA;
+  const ZR_GLOBAL TA* q = reinterpret_cast<const ZR_GLOBAL TA*>(p);
 #if ZR_NT_LOADS
-  return __builtin_nontemporal_load(p);
+  return __builtin_nontemporal_load(q);
 #else
-  return *p;
+  return *q;
 #endif
 }
-template <typename T>
+template <typename T, int A = 0>
 __device__ __forceinline__ void st_global(ZR_GLOBAL T* p, T v) {
+  typedef T __attribute__((aligned(A ? A : alignof(T)))) TA;
+  ZR_GLOBAL TA* q = reinterpret_cast<ZR_GLOBAL TA*>(p);
 #if ZR_NT_STORES
-  __builtin_nontemporal_store(v, p);
+  __builtin_nontemporal_store(v, q);
 #else
-  *p = v;
+  *q = v;
 #endif
 }
-template <typename T>
+template <typename T, int A = 0>
 __device__ __forceinline__ T ld_stream(const void* p) {
-  return ld_global<T>(gptr<T>(p));
+  return ld_global<T, A>(gptr<T>(p));
 }
-template <typename T>
+template <typename T, int A = 0>
 __device__ __forceinline__ void st_stream(void* p, T v) {
-  st_global<T>(gptr<T>(p), v);
+  st_global<T, A>(gptr<T>(p), v);
 }
 
 // Slot loads/stores relative to a per-tile stream base (uniform across the
 // workgroup) at a per-lane byte offset.
-template <typename V>
+template <typename V, int A = 0>
 __device__ __forceinline__ V ld_tile(uint64_t base, uint32_t off) {
   const ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<const void*>(base)) + off;
-  return ld_global<V>(reinterpret_cast<const ZR_GLOBAL V*>(b));
+  return ld_global<V, A>(reinterpret_cast<const ZR_GLOBAL V*>(b));
 }
-template <typename V>
+template <typename V, int A = 0>
 __device__ __forceinline__ void st_tile(uint64_t base, uint32_t off, V v) {
   ZR_GLOBAL char* b = gptr<char>(reinterpret_cast<void*>(base)) + off;
-  st_global<V>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
+  st_global<V, A>(reinterpret_cast<ZR_GLOBAL V*>(b), v);
 }
 
 // Four bf16 values that start 2 bytes into a dword (an odd element offset):
 // read the dwords that hold them (bytes -2 .. +10 of the slot, so one value
 // either side) and shift each pair down by 16 bits.  The caller keeps those
 // two extra values inside the segment.
-__device__ __forceinline__ u32x2d ld_bf16_odd(uint64_t base, uint32_t off) {
-  const u32x2d lo = ld_tile<u32x2d>(base - 2, off);
+__device__ __forceinline__ u32x2 ld_bf16_odd(uint64_t base, uint32_t off) {
+  const u32x2 lo = ld_tile<u32x2, kDW>(base - 2, off);
   const uint32_t hi = ld_tile<uint32_t>(base - 2, off + 8);
-  return u32x2d{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
+  return u32x2{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
                 __builtin_amdgcn_alignbit(hi, lo[1], 16)};
 }
 
 // The same for a 16-byte slot of eight bf16 values (the all-gather's slot).
-__device__ __forceinline__ u32x4d ld_bf16x8_odd(uint64_t base, uint32_t off) {
-  const u32x4d lo = ld_tile<u32x4d>(base - 2, off);
+__device__ __forceinline__ u32x4 ld_bf16x8_odd(uint64_t base, uint32_t off) {
+  const u32x4 lo = ld_tile<u32x4, kDW>(base - 2, off);
   const uint32_t hi = ld_tile<uint32_t>(base - 2, off + 16);
-  return u32x4d{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
+  return u32x4{__builtin_amdgcn_alignbit(lo[1], lo[0], 16),
                 __builtin_amdgcn_alignbit(lo[2], lo[1], 16),
                 __builtin_amdgcn_alignbit(lo[3], lo[2], 16),
                 __builtin_amdgcn_alignbit(hi, lo[3], 16)};
@@ -240,7 +255,6 @@ __host__ __device__ __forceinline__ bool aligned(uint64_t addr, uint64_t bytes) 
 template <typename InT> struct In;
 template <> struct In<uint16_t> {
   using Vec = u32x2;
-  using VecD = u32x2d;
   __device__ static __forceinline__ float widen(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
@@ -254,7 +268,6 @@ template <> struct In<uint16_t> {
 };
 template <> struct In<float> {
   using Vec = u32x4;
-  using VecD = u32x4d;
   __device__ static __forceinline__ float widen(float v) { return v; }
   template <typename V>
   __device__ static __forceinline__ void unpack(V w, float* x) {
@@ -295,9 +308,9 @@ __device__ __forceinline__ void adam_elem(const AdamConsts& k, float g,
 // bf16 param / reduced-gradient copies of that slot.  Each destination is a
 // per-tile stream base plus the slot's byte offset (o4 for fp32 streams, o2
 // for the bf16 param); a zero base means "not written".
-template <typename F4, typename U2 = u32x2>
+template <int A = 0>
 __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
-                                          F4 th, F4 mm, F4 vv,
+                                          f32x4 th, f32x4 mm, f32x4 vv,
                                           uint64_t master, uint64_t m, uint64_t v,
                                           uint64_t pbf16, uint64_t gout,
                                           uint32_t o4, uint32_t o2) {
@@ -309,12 +322,12 @@ __device__ __forceinline__ void adam_slot(const AdamConsts& k, const float* g,
     b[e] = vv[e];
     adam_elem(k, g[e], t[e], a[e], b[e]);
   }
-  st_tile<F4>(master, o4, F4{t[0], t[1], t[2], t[3]});
-  st_tile<F4>(m, o4, F4{a[0], a[1], a[2], a[3]});
-  st_tile<F4>(v, o4, F4{b[0], b[1], b[2], b[3]});
-  if (gout) st_tile<F4>(gout, o4, F4{g[0], g[1], g[2], g[3]});
+  st_tile<f32x4, A>(master, o4, f32x4{t[0], t[1], t[2], t[3]});
+  st_tile<f32x4, A>(m, o4, f32x4{a[0], a[1], a[2], a[3]});
+  st_tile<f32x4, A>(v, o4, f32x4{b[0], b[1], b[2], b[3]});
+  if (gout) st_tile<f32x4, A>(gout, o4, f32x4{g[0], g[1], g[2], g[3]});
   if (pbf16)
-    st_tile<U2>(pbf16, o2, U2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
+    st_tile<u32x2, A>(pbf16, o2, u32x2{bf16_rne(t[0]) | (bf16_rne(t[1]) << 16),
                                     bf16_rne(t[2]) | (bf16_rne(t[3]) << 16)});
 }
 
@@ -357,8 +370,14 @@ struct RedArgs {
 constexpr int kRedArgSegs = 2;
 // Tile range of the launches that use them (A/B measured: +0.7% on a
 // 108 us launch; slower below ~20 us; no gain to find on 10 ms launches).
-constexpr int64_t kRedArgSegsMinTiles = 16384;
-constexpr int64_t kRedArgSegsMaxTiles = 262144;
+#ifndef ZR_ARGSEGS_MIN_TILES
+#define ZR_ARGSEGS_MIN_TILES 16384
+#endif
+#ifndef ZR_ARGSEGS_MAX_TILES
+#define ZR_ARGSEGS_MAX_TILES 262144
+#endif
+constexpr int64_t kRedArgSegsMinTiles = ZR_ARGSEGS_MIN_TILES;
+constexpr int64_t kRedArgSegsMaxTiles = ZR_ARGSEGS_MAX_TILES;
 struct RedArgsS : RedArgs {
   Seg aseg[kRedArgSegs];
 };
@@ -401,7 +420,7 @@ __device__ __forceinline__ void reduce_slot(const RedArgs& a, const V* w, float*
 
 // Same for a run-time replica count (loads issued inside the rank loop).
 // kOdd: replicas whose bit is set in odd_mask are read with ld_bf16_odd.
-template <typename InT, bool kDiv, typename Vec, bool kOdd = false>
+template <typename InT, bool kDiv, typename Vec, bool kOdd = false, int A = 0>
 __device__ __forceinline__ void reduce_slot_rt(const RedArgs& a, int rr, int64_t f,
                                                float* acc, uint64_t odd_mask = 0) {
   const uint64_t off = static_cast<uint64_t>(f) * sizeof(InT);
@@ -409,7 +428,7 @@ __device__ __forceinline__ void reduce_slot_rt(const RedArgs& a, int rr, int64_t
     if constexpr (kOdd) {
       if ((odd_mask >> r) & 1u) return ld_bf16_odd(a.in[r] + off, 0);
     }
-    return ld_stream<Vec>(reinterpret_cast<const void*>(a.in[r] + off));
+    return ld_stream<Vec, A>(reinterpret_cast<const void*>(a.in[r] + off));
   };
   float x[4];
   In<InT>::unpack(load(0), x);
@@ -498,9 +517,8 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
 template <typename InT, int R, bool kDiv, bool kFused, bool kDword, bool kArgSegs>
 __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
     const std::conditional_t<kArgSegs, RedArgsS, RedArgs> a) {
-  using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
-  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
-  using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
+  using Vec = typename In<InT>::Vec;
+  constexpr int A = kDword ? kDW : 0;  // alignment the slot accesses may assume
   constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t>;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
   const int rr = R > 0 ? R : a.R;
@@ -627,7 +645,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
 
     // Issue every load of the tile's slots first.
     Vec w[kSlots][kRL];
-    F4 s0[kSlots], s1[kSlots], s2[kSlots];
+    f32x4 s0[kSlots], s1[kSlots], s2[kSlots];
     bool full[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
@@ -649,17 +667,17 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
                 if ((odd_mask >> r) & 1u)
                   w[u][r] = ld_bf16_odd(a.in[r] + in_off, slot * VE * sizeof(InT));
                 else
-                  w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+                  w[u][r] = ld_tile<Vec, A>(a.in[r] + in_off, slot * VE * sizeof(InT));
               } else {
-                w[u][r] = ld_tile<Vec>(a.in[r] + in_off, slot * VE * sizeof(InT));
+                w[u][r] = ld_tile<Vec, A>(a.in[r] + in_off, slot * VE * sizeof(InT));
               }
             }
           }
         }
         if constexpr (kFused) {
-          s0[u] = ld_tile<F4>(b_master, slot * 16);
-          s1[u] = ld_tile<F4>(b_m, slot * 16);
-          s2[u] = ld_tile<F4>(b_v, slot * 16);
+          s0[u] = ld_tile<f32x4, A>(b_master, slot * 16);
+          s1[u] = ld_tile<f32x4, A>(b_m, slot * 16);
+          s2[u] = ld_tile<f32x4, A>(b_v, slot * 16);
         }
       }
     }
@@ -676,12 +694,12 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
         } else if constexpr (R > 0) {
           reduce_slot<InT, R, kDiv>(a, w[u], g);
         } else {
-          reduce_slot_rt<InT, kDiv, Vec, kOddBf16>(a, rr, sg.flat + rel, g, odd_mask);
+          reduce_slot_rt<InT, kDiv, Vec, kOddBf16, A>(a, rr, sg.flat + rel, g, odd_mask);
         }
         if constexpr (!kFused) {
-          st_tile<F4>(b_out, slot * 16, F4{g[0], g[1], g[2], g[3]});
+          st_tile<f32x4, A>(b_out, slot * 16, f32x4{g[0], g[1], g[2], g[3]});
         } else {
-          adam_slot<F4, U2>(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
+          adam_slot<A>(a.ac, g, s0[u], s1[u], s2[u], b_master, b_m, b_v, b_pb, b_go,
                     slot * 16, slot * 8);
         }
       } else if (rel < sg.numel && rel + VE > 0) {
@@ -726,8 +744,7 @@ struct AdamArgs {
 // host launches that variant when the pointers are not all slot-aligned).
 template <bool kVec, bool kDword>
 __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
-  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
-  using U2 = std::conditional_t<kDword, u32x2d, u32x2>;
+  constexpr int A = kDword ? kDW : 0;  // alignment the slot accesses may assume
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const uint64_t t4 = static_cast<uint64_t>(t) * kAdamTileElems * 4;
     const uint64_t b_g = reinterpret_cast<uint64_t>(a.grad) + t4;
@@ -735,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
     const uint64_t b_m = reinterpret_cast<uint64_t>(a.m) + t4;
     const uint64_t b_v = reinterpret_cast<uint64_t>(a.v) + t4;
     const uint64_t b_pb = a.pbf16 ? reinterpret_cast<uint64_t>(a.pbf16) + t4 / 2 : 0;
-    F4 g[kAdamSlots], th[kAdamSlots], mm[kAdamSlots], vv[kAdamSlots];
+    f32x4 g[kAdamSlots], th[kAdamSlots], mm[kAdamSlots], vv[kAdamSlots];
     bool full[kAdamSlots];
 #pragma unroll
     for (int u = 0; u < kAdamSlots; ++u) {
@@ -743,10 +760,10 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
       const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       full[u] = kVec && j + VE <= a.n;
       if (full[u]) {
-        g[u] = ld_tile<F4>(b_g, slot * 16);
-        th[u] = ld_tile<F4>(b_master, slot * 16);
-        mm[u] = ld_tile<F4>(b_m, slot * 16);
-        vv[u] = ld_tile<F4>(b_v, slot * 16);
+        g[u] = ld_tile<f32x4, A>(b_g, slot * 16);
+        th[u] = ld_tile<f32x4, A>(b_master, slot * 16);
+        mm[u] = ld_tile<f32x4, A>(b_m, slot * 16);
+        vv[u] = ld_tile<f32x4, A>(b_v, slot * 16);
       }
     }
 #pragma unroll
@@ -755,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
       const int64_t j = t * kAdamTileElems + static_cast<int64_t>(slot) * VE;
       if (full[u]) {
         const float gg[4] = {g[u][0], g[u][1], g[u][2], g[u][3]};
-        adam_slot<F4, U2>(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
+        adam_slot<A>(a.ac, gg, th[u], mm[u], vv[u], b_master, b_m, b_v, b_pb, 0,
                           slot * 16, slot * 8);
       } else if (j < a.n) {
         const int64_t e1 = j + VE < a.n ? j + VE : a.n;
@@ -795,7 +812,8 @@ struct IpgArgs {
 // ld_bf16_odd.  The host launches that variant only for calls that need it.
 template <typename InT, bool kDword>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
-  using Vec = std::conditional_t<kDword, typename In<InT>::VecD, typename In<InT>::Vec>;
+  using Vec = typename In<InT>::Vec;
+  constexpr int A = kDword ? kDW : 0;  // alignment the gradient reads may assume
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const IpgSeg sg = a.seg[find_arg_seg(a.seg, a.nseg, t)];
     const int64_t lt = t - sg.tile0;
@@ -832,9 +850,9 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
           if (odd)
             x[u] = ld_bf16_odd(sg.src + rel * sizeof(InT), 0);
           else
-            x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+            x[u] = ld_stream<Vec, A>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
         } else {
-          x[u] = ld_stream<Vec>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
+          x[u] = ld_stream<Vec, A>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
         }
         cur[u] = ld_stream<f32x4>(a.main_grad + sg.dst + rel);
       }
@@ -876,7 +894,7 @@ struct CopyArgs {
 // dword-aligned; the host launches that variant only for calls that need it.
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
-  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
+  constexpr int A = kDword ? kDW : 0;  // alignment the source reads may assume
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
@@ -892,19 +910,19 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const CopyArgs a) {
         if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kCopyTileElems;
-    F4 x[kCopySlots];
+    f32x4 x[kCopySlots];
     bool full[kCopySlots];
 #pragma unroll
     for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= sg.numel;
-      if (full[u]) x[u] = ld_stream<F4>(s + rel);
+      if (full[u]) x[u] = ld_stream<f32x4, A>(s + rel);
     }
 #pragma unroll
     for (int u = 0; u < kCopySlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       if (full[u]) {
-        st_stream<F4>(d + rel, x[u]);
+        st_stream<f32x4>(d + rel, x[u]);
       } else if (rel < sg.numel && rel + VE > 0) {
         const int64_t e0 = rel < 0 ? 0 : rel;
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
@@ -928,7 +946,7 @@ struct RingArgs {
 
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
-  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
+  constexpr int A = kDword ? kDW : 0;  // alignment the source reads may assume
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
     const int64_t lt = t - static_cast<int64_t>(k) * a.tiles_per_rank;
@@ -947,7 +965,7 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
         if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingTileElems;
-    F4 x[kRingSlots];
+    f32x4 x[kRingSlots];
     f32x4 y[kRingSlots];
     bool full[kRingSlots];
 #pragma unroll
@@ -955,7 +973,7 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(const RingArgs a) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
       if (full[u]) {
-        x[u] = ld_stream<F4>(s + rel);
+        x[u] = ld_stream<f32x4, A>(s + rel);
         y[u] = ld_stream<f32x4>(d + rel);
       }
     }
@@ -1009,7 +1027,7 @@ __host__ __device__ constexpr int64_t gather_tile_elems() {
 // ld_bf16x8_odd; the host launches that variant only when needed.
 template <typename T, bool kDword>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
-  using LV = std::conditional_t<kDword, u32x4d, u32x4>;
+  constexpr int A = kDword ? kDW : 0;  // alignment the partition reads may assume
   constexpr int ES = sizeof(T);
   constexpr int GV = 16 / ES;                          // elements per slot
   constexpr int64_t TE = gather_tile_elems<T>();       // elements per tile
@@ -1044,10 +1062,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
         // ld_bf16x8_odd reads one value either side of the slot.
         const int64_t lo = odd ? 1 : 0;
         full[u] = vec && rel >= lo && rel + GV + lo <= sg.numel;
-        if (full[u]) x[u] = odd ? ld_bf16x8_odd(bs, slot * 16) : ld_tile<LV>(bs, slot * 16);
+        if (full[u]) x[u] = odd ? ld_bf16x8_odd(bs, slot * 16) : ld_tile<u32x4, A>(bs, slot * 16);
       } else {
         full[u] = vec && rel >= 0 && rel + GV <= sg.numel;
-        if (full[u]) x[u] = ld_tile<LV>(bs, slot * 16);
+        if (full[u]) x[u] = ld_tile<u32x4, A>(bs, slot * 16);
       }
     }
 #pragma unroll
@@ -1070,7 +1088,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const XArgs a) {
 // k-1's buffer into its own.
 template <bool kDword>
 __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
-  using F4 = std::conditional_t<kDword, f32x4d, f32x4>;
+  constexpr int A = kDword ? kDW : 0;  // alignment the source reads may assume
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
     const int k = static_cast<int>(t / a.tiles_per_rank);
     const int64_t lt = t - static_cast<int64_t>(k) * a.tiles_per_rank;
@@ -1089,13 +1107,13 @@ __global__ __launch_bounds__(kThreads) void ring_ag_kernel(const RingArgs a) {
         if (aligned(reinterpret_cast<uint64_t>(d + j), 16)) j0 = j;
     const bool vec = j0 >= 0;
     const int64_t rel0 = (j0 > 0 ? j0 - VE : 0) + lt * kRingAgTileElems;
-    F4 x[kRingAgSlots];
+    f32x4 x[kRingAgSlots];
     bool full[kRingAgSlots];
 #pragma unroll
     for (int u = 0; u < kRingAgSlots; ++u) {
       const int64_t rel = rel0 + static_cast<int64_t>(u * kThreads + threadIdx.x) * VE;
       full[u] = vec && rel >= 0 && rel + VE <= a.chunk;
-      if (full[u]) x[u] = ld_stream<F4>(s + rel);
+      if (full[u]) x[u] = ld_stream<f32x4, A>(s + rel);
     }
 #pragma unroll
     for (int u = 0; u < kRingAgSlots; ++u) {
@@ -1345,11 +1363,11 @@ zr_status launch_reduce_t(const RedArgsS& as, int R, bool div, bool dword, bool 
 #define ZR_LAUNCH(RR, DD)                                                           \
   do {                                                                              \
     if (dword)                                                                      \
-      reduce_kernel<InT, RR, DD, kFused, true, false><<<grid, kThreads, 0, st>>>(a);  \
+      ZR_KERNEL_LAUNCH(grid, kThreads, st, a, reduce_kernel<InT, RR, DD, kFused, true, false>);  \
     else if (argsegs)                                                               \
-      reduce_kernel<InT, RR, DD, kFused, false, true><<<grid, kThreads, 0, st>>>(as); \
+      ZR_KERNEL_LAUNCH(grid, kThreads, st, as, reduce_kernel<InT, RR, DD, kFused, false, true>); \
     else                                                                            \
-      reduce_kernel<InT, RR, DD, kFused, false, false><<<grid, kThreads, 0, st>>>(a); \
+      ZR_KERNEL_LAUNCH(grid, kThreads, st, a, reduce_kernel<InT, RR, DD, kFused, false, false>); \
   } while (0)
   if (div) {
     switch (R) {
@@ -1405,7 +1423,7 @@ zr_status stage_segments(const Seg* segs, int64_t n, Seg* table, hipStream_t str
     sa.n = static_cast<int32_t>(std::min<int64_t>(kStageSegs, n - b));
     for (int i = 0; i < sa.n; ++i) sa.seg[i] = segs[b + i];
     sa.out = table + b;
-    stage_segs_kernel<<<1, kStageSegs, 0, stream>>>(sa);
+    ZR_KERNEL_LAUNCH(1, kStageSegs, stream, sa, stage_segs_kernel);
     const zr_status st = check_launch("segment staging launch");
     if (st != ZR_OK) return st;
   }
@@ -1722,9 +1740,9 @@ extern "C" zr_status zr_adam_partition(const zr_adam* h, const float* grad, floa
     a.tile_base = launch_first(total, nl, i);
     a.tile_end = launch_first(total, nl, i + 1);
     const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
-    if (vec) adam_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
-    else if (dword) adam_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
-    else adam_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+    if (vec) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, adam_kernel<true, false>);
+    else if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, adam_kernel<true, true>);
+    else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, adam_kernel<false, false>);
     st = check_launch("adam_partition launch");
     if (st != ZR_OK) return st;
   }
@@ -1804,11 +1822,11 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
         a.tile_end = launch_first(tiles, nl, i + 1);
         const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
         if (grad_dtype == ZR_BF16) {
-          if (dword) ipg_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
-          else ipg_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+          if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, true>);
+          else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, false>);
         } else {
-          if (dword) ipg_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
-          else ipg_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+          if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, true>);
+          else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, false>);
         }
         st = check_launch("ipg_accumulate launch");
         if (st != ZR_OK) return st;
@@ -1866,8 +1884,8 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
       a.tile_base = launch_first(total, nl, i);
       a.tile_end = launch_first(total, nl, i + 1);
       const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
-      if (dword) copy_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-      else copy_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+      if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, copy_kernel<true>);
+      else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, copy_kernel<false>);
       st = check_launch("copy_grads_in_partition launch");
       if (st != ZR_OK) return st;
     }
@@ -1935,11 +1953,11 @@ extern "C" zr_status zr_all_gather_params(const zr_plan* plan, int32_t group,
       a.tile_end = launch_first(tiles, nl, i + 1);
       const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
       if (dtype == ZR_BF16) {
-        if (dword) gather_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
-        else gather_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+        if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, gather_kernel<uint16_t, true>);
+        else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, gather_kernel<uint16_t, false>);
       } else {
-        if (dword) gather_kernel<float, true><<<grid, kThreads, 0, stream>>>(a);
-        else gather_kernel<float, false><<<grid, kThreads, 0, stream>>>(a);
+        if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, gather_kernel<float, true>);
+        else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, gather_kernel<float, false>);
       }
       st = check_launch("all_gather_params launch");
       if (st != ZR_OK) return st;
@@ -2012,8 +2030,8 @@ extern "C" zr_status zr_ring_ag_step(float* const* rank_bufs, int32_t n_ranks,
     a.tile_base = launch_first(total, nl, i);
     a.tile_end = launch_first(total, nl, i + 1);
     const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
-    if (dword) ring_ag_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-    else ring_ag_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+    if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ring_ag_kernel<true>);
+    else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ring_ag_kernel<false>);
     st = check_launch("ring_ag_step launch");
     if (st != ZR_OK) return st;
   }
@@ -2037,8 +2055,8 @@ extern "C" zr_status zr_ring_rs_step(float* const* rank_bufs, int32_t n_ranks,
     a.tile_base = launch_first(total, nl, i);
     a.tile_end = launch_first(total, nl, i + 1);
     const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
-    if (dword) ring_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-    else ring_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+    if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ring_kernel<true>);
+    else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ring_kernel<false>);
     st = check_launch("ring_rs_step launch");
     if (st != ZR_OK) return st;
   }
