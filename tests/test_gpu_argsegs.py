@@ -7,12 +7,13 @@ table.  Reduced gradients bit-exact; Adam within rel 1e-6 / abs 1e-7 (v
 relative only); bf16 param = RNE of the kernel's own master.
 
 Which path a case takes follows from the library's launch rules, stated here
-so the cases can be checked by hand: a tile is 512 elements, a segment of n
-elements spans (n + 63 + 511) // 512 tiles, a selection of T tiles moving b
-bytes per tile is cut into ceil(T / floor(2^31 / b)) equal launches, and the
-argument path is taken when the selection has at most two segments, a launch
-spans 16,384-262,144 tiles and every stream shares a 16-byte (bf16: 8-byte)
-phase."""
+so the cases can be checked by hand: a tile is 256 elements for fp32 replicas
+and 512 for bf16, a segment of n elements spans (n + 63 + tile - 1) // tile
+tiles, a selection of T tiles moving b bytes per tile is cut into
+ceil(T / floor(2^31 / b)) equal launches, and the argument path is taken when
+the selection has at most two segments, a launch spans 8,388,608-134,217,728
+elements (its tiles times the tile size) and every stream shares a 16-byte
+(bf16: 8-byte) phase."""
 
 import gc
 
@@ -36,8 +37,8 @@ HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
 DEV = "cuda"
 
 
-def _tiles(n):
-    return (n + 63 + 511) // 512
+def _tiles(n, tile):
+    return (n + 63 + tile - 1) // tile
 
 
 def _launch_split(total_tiles, tile_bytes):
@@ -62,12 +63,13 @@ def _run(numels, R, B, dst, is_bf16, fused, seed, expect_segs, expect_launches, 
     pad = max(0, min(P, (dst + 1) * P - T))
     nseg = len(segs) + (1 if pad else 0)
     assert nseg == expect_segs
-    tiles = sum(_tiles(s.numel) for s in segs) + (_tiles(pad) if pad else 0)
     s_in = 2 if is_bf16 else 4
-    tile_bytes = 512 * (R * s_in + (30 if fused else 4))
+    tile = 512 if is_bf16 else 256
+    tiles = sum(_tiles(s.numel, tile) for s in segs) + (_tiles(pad, tile) if pad else 0)
+    tile_bytes = tile * (R * s_in + (30 if fused else 4))
     nl, per = _launch_split(tiles, tile_bytes)
     assert nl == expect_launches
-    assert (nseg <= 2 and 16384 <= per <= 262144) == expect_args
+    assert (nseg <= 2 and 16384 * 512 <= per * tile <= 262144 * 512) == expect_args
     # replica windows of partition dst, drawn on the device from seeds
     lo, n_real = dst * P, min(P, max(0, T - dst * P))
     dt = "bf16" if is_bf16 else "fp32"
@@ -102,7 +104,8 @@ def _run(numels, R, B, dst, is_bf16, fused, seed, expect_segs, expect_launches, 
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("is_bf16", [False, True])
 def test_one_segment_in_arguments(fused, is_bf16):
-    # one param of 4 x 9,000,000: partition 1 is one slice of 17,579 tiles
+    # one param of 4 x 9,000,000: partition 1 is one slice (35,157 fp32 tiles,
+    # 17,579 bf16 tiles)
     _run([36_000_000], 4, 1 << 40, 1, is_bf16, fused, 1, 1, 1, True)
     _free()
 
@@ -125,15 +128,16 @@ def test_two_segments_cut_by_a_bucket_border(fused, is_bf16):
 
 @pytest.mark.parametrize("fused", [True, False])
 def test_tile_threshold_both_sides(fused):
-    # 16,381 tiles: device table; 16,385 tiles: kernel arguments
+    # 32,762 fp32 tiles (8,387,072 elements): device table; 32,770 tiles
+    # (8,389,120 elements): kernel arguments
     _run([4 * 8_387_000], 4, 1 << 40, 2, False, fused, 4, 1, 1, False)
     _run([4 * 8_389_000], 4, 1 << 40, 2, False, fused, 5, 1, 1, True)
     _free()
 
 
 def test_two_launches_segments_in_arguments():
-    # fp32, 8 replicas, 40M-element partition: 78,126 tiles of 31,744 bytes
-    # (fused, reduced gradient written) -> two launches of 39,063 tiles
+    # fp32, 8 replicas, 40M-element partition: 156,251 tiles of 15,872 bytes
+    # (fused, reduced gradient written) -> two launches of 78,126 tiles
     _run([8 * 40_000_000], 8, 1 << 40, 2, False, True, 6, 1, 2, True)
     _free()
 

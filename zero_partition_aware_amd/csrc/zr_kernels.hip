@@ -76,8 +76,15 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 namespace {
 
 // Launch-shape constants (compile-time; the defaults are the tuned values).
-#ifndef ZR_TILE_ELEMS
-#define ZR_TILE_ELEMS 512
+// The reduce kernels (reduce-scatter, fused reduce + Adam) give each lane one
+// 4-element slot and take 1 KiB of every replica stream per tile: 256
+// elements on one wave for fp32 replicas, 512 on two waves for bf16
+// (red_threads below).  The other kernels use workgroups of ZR_THREADS lanes.
+#ifndef ZR_RED_THREADS_F32
+#define ZR_RED_THREADS_F32 64
+#endif
+#ifndef ZR_RED_THREADS_BF16
+#define ZR_RED_THREADS_BF16 128
 #endif
 #ifndef ZR_THREADS
 #define ZR_THREADS 128
@@ -102,15 +109,24 @@ namespace {
   __VA_ARGS__<<<(grid), (block), 0, (stream)>>>(args)
 #endif
 constexpr int kThreads = ZR_THREADS;
-constexpr int64_t kTileElems = ZR_TILE_ELEMS;
 constexpr int VE = 4;  // elements per lane slot
 // Cache-line size the reduce kernels align replica tiles to, and the largest
 // tile shift that alignment can need (a bf16 line minus one element).
 constexpr int64_t kLineBytes = 128;
 constexpr int64_t kMaxLineShift = kLineBytes / 2 - 1;
-constexpr int kSlots = static_cast<int>(kTileElems / (kThreads * VE));
-static_assert(kSlots >= 1 && kTileElems == int64_t(kSlots) * kThreads * VE,
-              "a tile must be a whole number of lane slots");
+// Lanes of a reduce-kernel workgroup and elements of its tile, by replica
+// element type.  A/B-measured, calls interleaved in one process: fp32 fused
+// on a 1.0e9-element share 6.15 TB/s with 256-element one-wave tiles against
+// 6.03 with 512-element two-wave tiles, on the 5.4e8-element MoE expert share
+// 6.13 against 6.00; bf16 fused on a 15.5M-element share 5.94 against 6.00.
+template <typename InT>
+__host__ __device__ constexpr int red_threads() {
+  return sizeof(InT) == 4 ? ZR_RED_THREADS_F32 : ZR_RED_THREADS_BF16;
+}
+template <typename InT>
+__host__ __device__ constexpr int64_t red_tile() {
+  return int64_t(red_threads<InT>()) * VE;
+}
 constexpr int kIpgMaxSegs = 48;
 // Slots per lane in the IPG kernel (its tiles are kIpgSlots lane slots of
 // every thread).
@@ -120,7 +136,7 @@ constexpr int kIpgMaxSegs = 48;
 constexpr int kIpgSlots = ZR_IPG_SLOTS;
 constexpr int64_t kIpgTileElems = int64_t(kIpgSlots) * kThreads * VE;
 // Slots per lane of the standalone Adam, segmented copy and ring-step kernels,
-// and the all-gather's tile size in units of kTileElems fp32 elements.  Each
+// and the all-gather's tile size in units of 512 fp32 elements.  Each
 // of these kernels covers kXSlots * kThreads * VE elements per tile.  Values
 // from A/B measurement: two slots pay for the light streams (copy +10%, ring
 // reduce-scatter step +2%, all-gather +2.5%, IPG +2.6%); Adam (-4%) and the
@@ -376,8 +392,10 @@ constexpr int kRedArgSegs = 2;
 #ifndef ZR_ARGSEGS_MAX_TILES
 #define ZR_ARGSEGS_MAX_TILES 262144
 #endif
-constexpr int64_t kRedArgSegsMinTiles = ZR_ARGSEGS_MIN_TILES;
-constexpr int64_t kRedArgSegsMaxTiles = ZR_ARGSEGS_MAX_TILES;
+// (The ranges are stated in 512-element tiles and applied as element counts,
+// so they keep their meaning for either tile shape.)
+constexpr int64_t kRedArgSegsMinElems = int64_t(ZR_ARGSEGS_MIN_TILES) * 512;
+constexpr int64_t kRedArgSegsMaxElems = int64_t(ZR_ARGSEGS_MAX_TILES) * 512;
 struct RedArgsS : RedArgs {
   Seg aseg[kRedArgSegs];
 };
@@ -515,12 +533,14 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
 // variant only for selections with a segment at which no phase is
 // slot-aligned, so the common instantiations carry none of its code.
 template <typename InT, int R, bool kDiv, bool kFused, bool kDword, bool kArgSegs>
-__global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
+__global__ __launch_bounds__(red_threads<InT>()) ZR_OCCUPANCY void reduce_kernel(
     const std::conditional_t<kArgSegs, RedArgsS, RedArgs> a) {
   using Vec = typename In<InT>::Vec;
   constexpr int A = kDword ? kDW : 0;  // alignment the slot accesses may assume
   constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t>;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
+  constexpr int kTH = red_threads<InT>();
+  constexpr int64_t kTile = red_tile<InT>();
   const int rr = R > 0 ? R : a.R;
 
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
@@ -621,7 +641,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
     }
     const bool vec = ph >= 0;
     const int64_t shift = vec ? (period - ph) % period : 0;
-    const int64_t rel0 = lt * kTileElems - shift;
+    const int64_t rel0 = lt * kTile - shift;
 
     // Per-tile stream bases: element rel0 of the segment in every stream.
     // spart + rel0 (and sg.flat + rel0) can be negative for a segment's
@@ -644,12 +664,13 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
     }
 
     // Issue every load of the tile's slots first.
+    constexpr int kSlots = 1;
     Vec w[kSlots][kRL];
     f32x4 s0[kSlots], s1[kSlots], s2[kSlots];
     bool full[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int slot = u * kTH + static_cast<int>(threadIdx.x);
       const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
       if constexpr (kOddBf16) {
         // ld_bf16_odd reads one value either side of the slot.
@@ -684,7 +705,7 @@ __global__ __launch_bounds__(kThreads) ZR_OCCUPANCY void reduce_kernel(
 
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-      const int slot = u * kThreads + static_cast<int>(threadIdx.x);
+      const int slot = u * kTH + static_cast<int>(threadIdx.x);
       const int64_t rel = rel0 + static_cast<int64_t>(slot) * VE;
       if (full[u]) {
         float g[4];
@@ -1015,7 +1036,7 @@ struct XArgs {
 // (bf16 patterns) or float.  Used by the parameter all-gather.  There is no
 // fp32 stream to match, so a slot is one 16-byte vector of either type
 // (8 bf16 or 4 fp32) and a tile holds kGatherTileBytes.
-constexpr int64_t kGatherTileBytes = kTileElems * 4 * ZR_GATHER_SLOTS;
+constexpr int64_t kGatherTileBytes = int64_t(kThreads) * VE * 4 * ZR_GATHER_SLOTS;
 template <typename T>
 __host__ __device__ constexpr int64_t gather_tile_elems() {
   return kGatherTileBytes / static_cast<int64_t>(sizeof(T));
@@ -1138,8 +1159,8 @@ int64_t tiles_for(int64_t numel, int64_t tile) {
 }
 // Reduce-kernel segments may start their tiles up to kMaxLineShift elements
 // early (line-aligned replica tiles); the count covers the largest shift.
-int64_t reduce_tiles_for(int64_t numel) {
-  return (numel + kMaxLineShift + kTileElems - 1) / kTileElems;
+int64_t reduce_tiles_for(int64_t numel, int64_t tile) {
+  return (numel + kMaxLineShift + tile - 1) / tile;
 }
 
 // Launch tables derived from a plan: the host segment list (pure host data,
@@ -1152,9 +1173,9 @@ struct DevTable {
   int device = 0;
 };
 enum TableKind { kReduceTable = 0, kCopyTable = 1 };
-// kind, group, first bucket, end bucket (exclusive), dst
-using HostKey = std::tuple<int, int32_t, int64_t, int64_t, int32_t>;
-using DevKey = std::tuple<int, int, int32_t, int64_t, int64_t, int32_t>;  // device + HostKey
+// kind, group, first bucket, end bucket (exclusive), dst, tile elements
+using HostKey = std::tuple<int, int32_t, int64_t, int64_t, int32_t, int64_t>;
+using DevKey = std::tuple<int, int, int32_t, int64_t, int64_t, int32_t, int64_t>;  // device + HostKey
 
 struct DevCache {
   std::mutex mu;
@@ -1235,7 +1256,7 @@ int64_t launch_first(int64_t total, int64_t n, int64_t i) { return total * i / n
 // bucket
 // (reduce tables only); each gets its tile offset.
 std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
-                                int64_t first, int64_t last, int32_t dst) {
+                                int64_t first, int64_t last, int32_t dst, int64_t tile) {
   std::vector<Seg> out;
   const int64_t a = plan->bucket_first[first];
   const int64_t b = plan->bucket_first[last];
@@ -1269,7 +1290,7 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
   int64_t tiles = 0;
   for (auto& g : out) {
     g.tile0 = tiles;
-    tiles += kind == kReduceTable ? reduce_tiles_for(g.numel) : tiles_for(g.numel, kCopyTileElems);
+    tiles += kind == kReduceTable ? reduce_tiles_for(g.numel, tile) : tiles_for(g.numel, tile);
   }
   Seg sentinel{};
   sentinel.tile0 = tiles;
@@ -1279,15 +1300,15 @@ std::vector<Seg> build_segments(const zr_plan* plan, int kind, int32_t group,
 
 // Host segment list for a call (no HIP call is made).
 zr_status get_host_table(const zr_plan* plan, int kind, int32_t group, int64_t first,
-                         int64_t last, int32_t dst, const std::vector<Seg>** out) {
+                         int64_t last, int32_t dst, int64_t tile, const std::vector<Seg>** out) {
   DevCache* c = cache_of(plan);
   std::lock_guard<std::mutex> lk(c->mu);
-  const HostKey key{kind, group, first, last, dst};
+  const HostKey key{kind, group, first, last, dst, tile};
   auto it = c->host.find(key);
   if (it == c->host.end()) {
     HostTable t;
     try {
-      t.segs = build_segments(plan, kind, group, first, last, dst);
+      t.segs = build_segments(plan, kind, group, first, last, dst, tile);
     } catch (const std::bad_alloc&) {
       return fail(ZR_ERR_OOM, "out of host memory building a launch table");
     }
@@ -1299,11 +1320,12 @@ zr_status get_host_table(const zr_plan* plan, int kind, int32_t group, int64_t f
 
 // Device copy of the same list on `device` (synchronous upload on first use).
 zr_status get_dev_table(const zr_plan* plan, int kind, int32_t group, int64_t first,
-                        int64_t last, int32_t dst, int device, const std::vector<Seg>& host,
+                        int64_t last, int32_t dst, int64_t tile, int device,
+                        const std::vector<Seg>& host,
                         const Seg** out) {
   DevCache* c = cache_of(plan);
   std::lock_guard<std::mutex> lk(c->mu);
-  const DevKey key{device, kind, group, first, last, dst};
+  const DevKey key{device, kind, group, first, last, dst, tile};
   auto it = c->dev.find(key);
   if (it != c->dev.end()) {
     *out = it->second.dev;
@@ -1363,11 +1385,11 @@ zr_status launch_reduce_t(const RedArgsS& as, int R, bool div, bool dword, bool 
 #define ZR_LAUNCH(RR, DD)                                                           \
   do {                                                                              \
     if (dword)                                                                      \
-      ZR_KERNEL_LAUNCH(grid, kThreads, st, a, reduce_kernel<InT, RR, DD, kFused, true, false>);  \
+      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, a, reduce_kernel<InT, RR, DD, kFused, true, false>);  \
     else if (argsegs)                                                               \
-      ZR_KERNEL_LAUNCH(grid, kThreads, st, as, reduce_kernel<InT, RR, DD, kFused, false, true>); \
+      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, as, reduce_kernel<InT, RR, DD, kFused, false, true>); \
     else                                                                            \
-      ZR_KERNEL_LAUNCH(grid, kThreads, st, a, reduce_kernel<InT, RR, DD, kFused, false, false>); \
+      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, a, reduce_kernel<InT, RR, DD, kFused, false, false>); \
   } while (0)
   if (div) {
     switch (R) {
@@ -1485,7 +1507,9 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     }
   }
   const std::vector<Seg>* hs = nullptr;
-  zr_status st = get_host_table(plan, kReduceTable, group, first, last, dst, &hs);
+  // Tile shape of this call's kernels (by replica element type).
+  const int64_t tile = dt == ZR_BF16 ? red_tile<uint16_t>() : red_tile<float>();
+  zr_status st = get_host_table(plan, kReduceTable, group, first, last, dst, tile, &hs);
   if (st != ZR_OK) return st;
   const int nseg = static_cast<int>(hs->size()) - 1;
   // Every replica window must cover every slice this call reads.
@@ -1546,15 +1570,15 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
   // Bytes one tile moves (the replicas, plus the partition output or the
   // Adam state), which sets how many launches the selection is cut into.
   const int64_t tile_bytes =
-      kTileElems * (static_cast<int64_t>(gi.world) * static_cast<int64_t>(s) +
+      tile * (static_cast<int64_t>(gi.world) * static_cast<int64_t>(s) +
                     (fused ? 26 + (gout ? 4 : 0) : 4));
   const int64_t nl = launches_for(total, tile_bytes);
   const int64_t per = (total + nl - 1) / nl;
   // Mid-sized launches over few segments carry their segments in the kernel
   // arguments (short launches measured faster with the device table); only
   // the other calls need the device table.
-  const bool argsegs = !dword && nseg <= kRedArgSegs && per >= kRedArgSegsMinTiles &&
-                       per <= kRedArgSegsMaxTiles;
+  const bool argsegs = !dword && nseg <= kRedArgSegs && per * tile >= kRedArgSegsMinElems &&
+                       per * tile <= kRedArgSegsMaxElems;
   if (!argsegs && noalloc) {
     Seg* table = nullptr;
     st = scratch_for(device, &table);
@@ -1563,7 +1587,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     if (st != ZR_OK) return st;
     a.segs = table;
   } else if (!argsegs) {
-    st = get_dev_table(plan, kReduceTable, group, first, last, dst, device, *hs, &a.segs);
+    st = get_dev_table(plan, kReduceTable, group, first, last, dst, tile, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
   RedArgsS as;
@@ -1855,7 +1879,7 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
         !elem_aligned(part_out, 4))
       return fail(ZR_ERR_INVALID, "buffers are null or not element-aligned");
     const std::vector<Seg>* hs = nullptr;
-    zr_status st = get_host_table(plan, kCopyTable, group, bucket, bucket + 1, dst, &hs);
+    zr_status st = get_host_table(plan, kCopyTable, group, bucket, bucket + 1, dst, kCopyTileElems, &hs);
     if (st != ZR_OK) return st;
     const int nseg = static_cast<int>(hs->size()) - 1;
     if (nseg == 0) return ZR_OK;
@@ -1863,7 +1887,8 @@ extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t gro
     st = device_info(&device, &cus);
     if (st != ZR_OK) return st;
     CopyArgs a{};
-    st = get_dev_table(plan, kCopyTable, group, bucket, bucket + 1, dst, device, *hs, &a.segs);
+    st = get_dev_table(plan, kCopyTable, group, bucket, bucket + 1, dst, kCopyTileElems, device, *hs,
+                       &a.segs);
     if (st != ZR_OK) return st;
     a.src = bucket_layout_src;
     a.dst = part_out;
