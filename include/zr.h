@@ -150,17 +150,31 @@ zr_status zr_plan_buckets(const zr_param* params, int64_t n_params,
  * while kernels that use it are still queued; it must not be used again. */
 void zr_plan_free(zr_plan* plan);
 
+/* Plan queries.  Each reads the plan only; ZR_ERR_INVALID for a null plan or
+ * output pointer or an index out of range.
+ *
+ * Number of buckets: the list's elements in order, cut every
+ * reduce_bucket_size elements ([ZeRO-RS blog §五] reduce_bucket_size; §四 the
+ * IPG bucket the gradients fill). */
 zr_status zr_plan_num_buckets(const zr_plan* plan, int64_t* out);
+/* Number of params in the list the plan was built from. */
 zr_status zr_plan_num_params(const zr_plan* plan, int64_t* out);
+/* The recorded stage flag, 0 = ZeRO-1, 1 = ZeRO-2 ([ZeRO-RS blog §三.1]
+ * partition_gradients). */
 zr_status zr_plan_partition_gradients(const zr_plan* plan, int32_t* out);
 
 /* Group g's sizes: total T_g, padded L_g, partition P_g = L_g / R_g, and the
- * divisor D_g = R_g / sp_g as a float.  Any output pointer may be null. */
+ * divisor D_g = R_g / sp_g as a float ([ZeRO-RS blog §二] equal partitions of
+ * the padded flat space; §六 the mean over dp_world_size / sp_size, and the
+ * expert-parallel group reduced over its own ranks).  Any output pointer may
+ * be null. */
 zr_status zr_plan_group_info(const zr_plan* plan, int32_t g, int64_t* total,
                              int64_t* padded, int64_t* part_numel,
                              float* divisor);
 
-/* Offset o_p of param p inside its group's flat space. */
+/* Offset o_p of param p inside its group's flat space: the params of a group
+ * laid end to end in list order ([ZeRO-RS blog §二] the flattened parameter
+ * space; [Megatron DP] "梯度缓冲区+分桶+overlap" one contiguous buffer). */
 zr_status zr_plan_param_offset(const zr_plan* plan, int64_t p, int64_t* out);
 
 /* param_to_partition_ids[p] ([ZeRO-RS blog §三.2]): the partitions the param
@@ -182,7 +196,10 @@ zr_status zr_plan_param_buckets(const zr_plan* plan, int64_t p, int64_t* first,
                                 int64_t* last);
 
 /* The merged slices of one bucket (bucket >= 0) or of all buckets
- * (bucket == -1), in bucket order.  *s points into the plan. */
+ * (bucket == -1), in bucket order: each piece of a param inside a bucket,
+ * cut at partition borders, tagged with its destination rank, and adjacent
+ * pieces with the same (group, destination) merged ([ZeRO-RS blog §三.2] the
+ * slicing and merging of average_tensor).  *s points into the plan. */
 zr_status zr_plan_slices(const zr_plan* plan, int64_t bucket,
                          const zr_slice** s, int64_t* n);
 
