@@ -835,7 +835,7 @@ def setup_moe(torch, zr, workloads):
         {f"fused_g{g}": gr["bytes"] for g, gr in enumerate(groups)}, "fused_g1", cpu_leg
 
 
-def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
+def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False, fused=False):
     """The MoE step through the bucketed path of the pages' IPG design, for
     rank 0 of each group: reduce-scatter calls into the rank's fp32 gradient
     partitions (269 buckets of 5e6 elements, both groups interleaved), then
@@ -843,8 +843,13 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
     completed since the previous one (zr_reduce_scatter_local_range), a call
     per group after each layer's 17 parameters, taken in list order as the
     ready order; with ``per_bucket`` one call per (bucket, group) holding
-    slices for the rank.  With ``graph`` the whole step is captured once in a
-    HIP graph (torch.cuda.CUDAGraph) and each step is one replay."""
+    slices for the rank.  With ``fused`` each range call also applies Adam to
+    the partition elements it reduces (zr_reduce_scatter_adam_range): Adam is
+    elementwise, so updating an element as soon as its reduced gradient
+    exists gives the same numbers as one Adam pass after the last bucket, and
+    the reduced gradient never goes through HBM.  With ``graph`` the whole
+    step is captured once in a HIP graph (torch.cuda.CUDAGraph) and each step
+    is one replay."""
     name = "moe-16l"
     w = workloads.get(name)
     plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
@@ -862,7 +867,7 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
                            master=master, m=torch.zeros_like(master),
                            v=torch.zeros_like(master),
                            pbf16=torch.empty(P, dtype=torch.bfloat16, device="cuda")))
-        total_bytes += (R * 4 + 4 + 30) * P
+        total_bytes += (R * 4 + 26 if fused else R * 4 + 4 + 30) * P
     if per_bucket:
         # (bucket, group) selections holding slices for rank k, plus the last
         # bucket of every group (it also writes the group's padding).
@@ -887,6 +892,13 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
         assert done == nb
 
     def eager(t, timer):
+        if fused:
+            for g, b, n in calls:
+                gr = groups[g]
+                timer.launch(lambda: zr.zr_reduce_scatter_adam_range(
+                    plan, g, b, n, k, gr["reps"], gr["master"], gr["m"], gr["v"], gr["pbf16"],
+                    step=t, **HP), "fused")
+            return
         for g, b, n in calls:
             gr = groups[g]
             timer.launch(lambda: zr.zr_reduce_scatter_local_range(plan, g, b, n, k, gr["reps"],
@@ -897,20 +909,24 @@ def setup_moe_bucketed(torch, zr, workloads, graph=False, per_bucket=False):
                          "adam")
 
     # Per-call bytes of each kind, averaged over the step's calls of it.
-    launch_bytes = {"reduce": round(sum((gr["R"] * 4 + 4) * gr["P"] for gr in groups) / len(calls)),
-                    "adam": round(sum(30 * gr["P"] for gr in groups) / len(groups))}
+    if fused:
+        launch_bytes = {"fused": round(total_bytes / len(calls))}
+    else:
+        launch_bytes = {"reduce": round(sum((gr["R"] * 4 + 4) * gr["P"] for gr in groups) /
+                                        len(calls)),
+                        "adam": round(sum(30 * gr["P"] for gr in groups) / len(groups))}
     cfg = {"workload": name + ("-per-bucket" if per_bucket else "-bucketed") +
-           ("-graph" if graph else ""),
+           ("-fused" if fused else "") + ("-graph" if graph else ""),
            "params": len(w.numels), "groups": w.groups, "rank": k,
            "reduce_bucket_size": w.reduce_bucket_size, "buckets": nb,
            "trigger": "one call per (bucket, group) with slices for the rank" if per_bucket
            else "after each layer, one call per group for the buckets completed since the last",
-           "reduce_calls_per_step": len(calls), "adam_calls_per_step": len(groups),
+           "reduce_calls_per_step": len(calls), "adam_calls_per_step": 0 if fused else len(groups),
            "partition_elems": [gr["P"] for gr in groups], "grad_dtype": "fp32",
            "bytes_per_step": total_bytes, "launch_sizes": "mixed"}
     if not graph:
         return (lambda i, timer: eager(i + 1, timer)), total_bytes, \
-            sum(gr["P"] for gr in groups), cfg, launch_bytes, "reduce", None
+            sum(gr["P"] for gr in groups), cfg, launch_bytes, "fused" if fused else "reduce", None
 
     # Capture one step (Adam step number fixed at capture) after an eager
     # step has built the plan's launch tables.
@@ -1174,7 +1190,7 @@ def main():
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
                              "llama3-8b-overlap",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
-                             "moe-16l-per-bucket", "moe-16l-per-bucket-graph",
+                             "moe-16l-bucketed-fused", "moe-16l-per-bucket", "moe-16l-per-bucket-graph",
                              "llama3-8b-copy", "gpt2-small-all-ranks",
                              "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1220,6 +1236,7 @@ def main():
               "gpt2-small-copy": lambda *a: setup_gpt2_unfused(*a, copy_only=True),
               "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
               "moe-16l-bucketed": setup_moe_bucketed,
+              "moe-16l-bucketed-fused": lambda *a: setup_moe_bucketed(*a, fused=True),
               "llama3-8b-copy": setup_llama_copy,
               "gpt2-small-all-ranks": lambda *a: setup_gpt2(*a, all_ranks=True),
               "moe-16l-per-bucket": lambda *a: setup_moe_bucketed(*a, per_bucket=True),

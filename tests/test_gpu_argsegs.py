@@ -7,8 +7,8 @@ table.  Reduced gradients bit-exact; Adam within rel 1e-6 / abs 1e-7 (v
 relative only); bf16 param = RNE of the kernel's own master.
 
 Which path a case takes follows from the library's launch rules, stated here
-so the cases can be checked by hand: a tile is 256 elements for fp32 replicas
-and 512 for bf16, a segment of n elements spans (n + 63 + tile - 1) // tile
+so the cases can be checked by hand: a tile is 512 elements for the bf16
+fused step and 256 otherwise, a segment of n elements spans (n + 63 + tile - 1) // tile
 tiles, a selection of T tiles moving b bytes per tile is cut into
 ceil(T / floor(2^31 / b)) equal launches, and the argument path is taken when
 the selection has at most two segments, a launch spans 8,388,608-134,217,728
@@ -64,7 +64,7 @@ def _run(numels, R, B, dst, is_bf16, fused, seed, expect_segs, expect_launches, 
     nseg = len(segs) + (1 if pad else 0)
     assert nseg == expect_segs
     s_in = 2 if is_bf16 else 4
-    tile = 512 if is_bf16 else 256
+    tile = 512 if is_bf16 and fused else 256
     tiles = sum(_tiles(s.numel, tile) for s in segs) + (_tiles(pad, tile) if pad else 0)
     tile_bytes = tile * (R * s_in + (30 if fused else 4))
     nl, per = _launch_split(tiles, tile_bytes)
@@ -104,8 +104,8 @@ def _run(numels, R, B, dst, is_bf16, fused, seed, expect_segs, expect_launches, 
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("is_bf16", [False, True])
 def test_one_segment_in_arguments(fused, is_bf16):
-    # one param of 4 x 9,000,000: partition 1 is one slice (35,157 fp32 tiles,
-    # 17,579 bf16 tiles)
+    # one param of 4 x 9,000,000: partition 1 is one slice (35,157 tiles of
+    # 256 elements, 17,579 of 512 for the bf16 fused step)
     _run([36_000_000], 4, 1 << 40, 1, is_bf16, fused, 1, 1, 1, True)
     _free()
 

@@ -77,14 +77,17 @@ namespace {
 
 // Launch-shape constants (compile-time; the defaults are the tuned values).
 // The reduce kernels (reduce-scatter, fused reduce + Adam) give each lane one
-// 4-element slot and take 1 KiB of every replica stream per tile: 256
-// elements on one wave for fp32 replicas, 512 on two waves for bf16
+// 4-element slot: 256 elements on one wave for fp32 replicas and for the
+// bf16 reduce-scatter, 512 on two waves for the bf16 fused step
 // (red_threads below).  The other kernels use workgroups of ZR_THREADS lanes.
 #ifndef ZR_RED_THREADS_F32
 #define ZR_RED_THREADS_F32 64
 #endif
 #ifndef ZR_RED_THREADS_BF16
 #define ZR_RED_THREADS_BF16 128
+#endif
+#ifndef ZR_RED_THREADS_BF16_UNFUSED
+#define ZR_RED_THREADS_BF16_UNFUSED 64
 #endif
 #ifndef ZR_THREADS
 #define ZR_THREADS 128
@@ -115,17 +118,20 @@ constexpr int VE = 4;  // elements per lane slot
 constexpr int64_t kLineBytes = 128;
 constexpr int64_t kMaxLineShift = kLineBytes / 2 - 1;
 // Lanes of a reduce-kernel workgroup and elements of its tile, by replica
-// element type.  A/B-measured, calls interleaved in one process: fp32 fused
-// on a 1.0e9-element share 6.15 TB/s with 256-element one-wave tiles against
-// 6.03 with 512-element two-wave tiles, on the 5.4e8-element MoE expert share
-// 6.13 against 6.00; bf16 fused on a 15.5M-element share 5.94 against 6.00.
-template <typename InT>
+// element type and kernel.  A/B-measured, calls interleaved in one process:
+// fp32 fused on a 1.0e9-element share 6.15 TB/s with 256-element one-wave
+// tiles against 6.03 with 512-element two-wave tiles, on the 5.4e8-element
+// MoE expert share 6.13 against 6.00; bf16 fused on a 15.5M-element share
+// 5.94 against 6.00, the bf16 reduce-scatter on the same share 6.04 against
+// 5.96.
+template <typename InT, bool kFused>
 __host__ __device__ constexpr int red_threads() {
-  return sizeof(InT) == 4 ? ZR_RED_THREADS_F32 : ZR_RED_THREADS_BF16;
+  return sizeof(InT) == 4 ? ZR_RED_THREADS_F32
+                          : (kFused ? ZR_RED_THREADS_BF16 : ZR_RED_THREADS_BF16_UNFUSED);
 }
-template <typename InT>
+template <typename InT, bool kFused>
 __host__ __device__ constexpr int64_t red_tile() {
-  return int64_t(red_threads<InT>()) * VE;
+  return int64_t(red_threads<InT, kFused>()) * VE;
 }
 constexpr int kIpgMaxSegs = 48;
 // Slots per lane in the IPG kernel (its tiles are kIpgSlots lane slots of
@@ -533,14 +539,14 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
 // variant only for selections with a segment at which no phase is
 // slot-aligned, so the common instantiations carry none of its code.
 template <typename InT, int R, bool kDiv, bool kFused, bool kDword, bool kArgSegs>
-__global__ __launch_bounds__(red_threads<InT>()) ZR_OCCUPANCY void reduce_kernel(
+__global__ __launch_bounds__((red_threads<InT, kFused>())) ZR_OCCUPANCY void reduce_kernel(
     const std::conditional_t<kArgSegs, RedArgsS, RedArgs> a) {
   using Vec = typename In<InT>::Vec;
   constexpr int A = kDword ? kDW : 0;  // alignment the slot accesses may assume
   constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t>;
   constexpr int kRL = R > 0 ? R : 1;  // replica vectors held per slot
-  constexpr int kTH = red_threads<InT>();
-  constexpr int64_t kTile = red_tile<InT>();
+  constexpr int kTH = red_threads<InT, kFused>();
+  constexpr int64_t kTile = red_tile<InT, kFused>();
   const int rr = R > 0 ? R : a.R;
 
   for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
@@ -1382,14 +1388,18 @@ template <typename InT, bool kFused>
 zr_status launch_reduce_t(const RedArgsS& as, int R, bool div, bool dword, bool argsegs,
                           unsigned grid, hipStream_t st) {
   const RedArgs& a = as;
-#define ZR_LAUNCH(RR, DD)                                                           \
-  do {                                                                              \
-    if (dword)                                                                      \
-      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, a, reduce_kernel<InT, RR, DD, kFused, true, false>);  \
-    else if (argsegs)                                                               \
-      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, as, reduce_kernel<InT, RR, DD, kFused, false, true>); \
-    else                                                                            \
-      ZR_KERNEL_LAUNCH(grid, red_threads<InT>(), st, a, reduce_kernel<InT, RR, DD, kFused, false, false>); \
+#define ZR_LAUNCH(RR, DD)                                                      \
+  do {                                                                         \
+    constexpr int kTH = red_threads<InT, kFused>();                            \
+    if (dword)                                                                 \
+      ZR_KERNEL_LAUNCH(grid, kTH, st, a,                                       \
+                       reduce_kernel<InT, RR, DD, kFused, true, false>);       \
+    else if (argsegs)                                                          \
+      ZR_KERNEL_LAUNCH(grid, kTH, st, as,                                      \
+                       reduce_kernel<InT, RR, DD, kFused, false, true>);       \
+    else                                                                       \
+      ZR_KERNEL_LAUNCH(grid, kTH, st, a,                                       \
+                       reduce_kernel<InT, RR, DD, kFused, false, false>);      \
   } while (0)
   if (div) {
     switch (R) {
@@ -1507,8 +1517,10 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     }
   }
   const std::vector<Seg>* hs = nullptr;
-  // Tile shape of this call's kernels (by replica element type).
-  const int64_t tile = dt == ZR_BF16 ? red_tile<uint16_t>() : red_tile<float>();
+  // Tile shape of this call's kernels (by replica element type and kernel).
+  const int64_t tile = dt != ZR_BF16 ? red_tile<float, true>()
+                       : fused       ? red_tile<uint16_t, true>()
+                                     : red_tile<uint16_t, false>();
   zr_status st = get_host_table(plan, kReduceTable, group, first, last, dst, tile, &hs);
   if (st != ZR_OK) return st;
   const int nseg = static_cast<int>(hs->size()) - 1;
