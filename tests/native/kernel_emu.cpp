@@ -207,6 +207,9 @@ void reduce_case(Rng& r, int seed) {
   if (mode == 2) { first = r.uni(0, pl.nb - 1); last = r.uni(first, pl.nb); }
   const bool fused = r.uni(0, 1) == 1;
   const bool noalloc = fused && r.uni(0, 3) == 0 && mode != 2;
+  // the grid-capped fused call (a grid-stride walk of the tiles)
+  const int32_t cap = fused && !noalloc && mode != 2 && r.uni(0, 4) == 0
+                          ? static_cast<int32_t>(r.uni(1, 40)) : 0;
   // replicas: the whole flat space, or (one destination) its window
   const bool window = dst >= 0 && r.uni(0, 1) == 1;
   const int64_t base = window ? std::min<int64_t>(dst * gi.P, gi.T) : 0;
@@ -307,6 +310,9 @@ void reduce_case(Rng& r, int seed) {
     else if (noalloc)
       st = zr_reduce_scatter_adam_noalloc(pl.h, g, mode == 0 ? -1 : first, dst, zreps.data(), dt, &h,
                                           th.f(), m.f(), v.f(), pbp, gop, nullptr);
+    else if (cap > 0)
+      st = zr_reduce_scatter_adam_capped(pl.h, g, mode == 0 ? -1 : first, dst, zreps.data(), dt, &h,
+                                         th.f(), m.f(), v.f(), pbp, gop, cap, nullptr);
     else
       st = zr_reduce_scatter_adam(pl.h, g, mode == 0 ? -1 : first, dst, zreps.data(), dt, &h,
                                   th.f(), m.f(), v.f(), pbp, gop, nullptr);

@@ -3,7 +3,8 @@ UndefinedBehaviorSanitizer: the library's own sources (zr_kernels.hip compiled
 as C++ against tests/native/emu, the planner) driven through the C ABI by
 tests/native/kernel_emu.cpp on random plans, selections, element types,
 windows and pointer offsets, with tiny launch caps so that small cases take
-the multi-launch, argument-segment and device-table paths.  Any access
+the multi-launch, argument-segment and device-table paths, and a short
+XCD-weighted tile cycle so that they take its idle slots too.  Any access
 outside a buffer (vector accesses to the byte, scalar ones at ASan's
 granularity), any store before a buffer, and any output that differs from a
 plain loop over the plan's slices fails the run.  The coverage report must
@@ -33,6 +34,9 @@ def _build(tmp_path, kernels_src, name):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-ffp-contract=off",
            "-Wno-align-mismatch", "-D__HIP_PLATFORM_AMD__", "-DZR_LAUNCH_BYTES=65536",
            "-DZR_ARGSEGS_MIN_TILES=2", "-DZR_ARGSEGS_MAX_TILES=64",
+           # an XCD-weighted order of 2-round cycles from 4 replicas up, so
+           # that short launches hold whole cycles and both orders run
+           "-DZR_XCD_SKEW=2", "-DZR_XCD_SKEW_MIN_WORLD=4",
            "-I", os.path.join(NATIVE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-I", "/opt/rocm/include",
            "-x", "c++", kernels_src, "-x", "none", os.path.join(CSRC, "zr_plan.cpp"),

@@ -364,6 +364,46 @@ struct Seg {
   int32_t pad;    // 1: padding -- gradient 0, no replica is read
 };
 
+// XCD-weighted tile order.  The dispatcher deals a launch's workgroups to
+// the 8 XCDs in turn (workgroup b runs on XCD b % 8), and each XCD then works
+// through its share at its own pace; measured on MI355X with a probe that
+// records each workgroup's XCD and start time, the odd XCDs stream 2-7%
+// slower than the even ones on the fused step's access pattern, so with
+// equal shares the even XCDs idle at the end of every launch while the odd
+// ones finish.  In every round of ZR_XCD_SKEW x 8 workgroups the last
+// round's odd-slot workgroups take no tile, which gives the odd XCDs
+// (K-1)/K of the even XCDs' tiles while every XCD still walks the tiles in
+// address order.  0 = equal shares.  A/B-measured, calls interleaved in one
+// process on two machines, K = 32 against equal shares: 8 fp32 replicas on
+// the 1.0e9-element share +0.3-0.7%, 8 bf16 replicas fused on the
+// 15.5M-element share +0.75-1.0%, the 8-replica bf16 reduce-scatter
+// +1.9-2.0%, but the 2-replica fp32 MoE expert call -1.3%; so the order is
+// taken by selections of at least ZR_XCD_SKEW_MIN_WORLD replicas.
+#ifndef ZR_XCD_SKEW
+#define ZR_XCD_SKEW 32
+#endif
+#ifndef ZR_XCD_SKEW_MIN_WORLD
+#define ZR_XCD_SKEW_MIN_WORLD 8
+#endif
+constexpr int kXcdSkew = ZR_XCD_SKEW;
+// Tile offset (within the launch) of workgroup b, or -1 for no tile.
+__host__ __device__ inline int64_t skew_tile(uint32_t b) {
+  constexpr uint32_t per = 8u * (kXcdSkew > 0 ? kXcdSkew : 1), tiles_per = per - 4;
+  const uint32_t sr = b / per, rem = b % per, q = rem >> 3, x = rem & 7;
+  const int64_t base = static_cast<int64_t>(sr) * tiles_per;
+  if (q + 1 < static_cast<uint32_t>(kXcdSkew)) return base + q * 8 + x;
+  if (x & 1) return -1;
+  return base + (kXcdSkew - 1) * 8 + (x >> 1);
+}
+// Workgroups a launch of n tiles needs in that order: up to and including
+// the one that holds tile n - 1 (so n <= 8 (K - 1) tiles take n workgroups).
+inline int64_t skew_grid(int64_t n) {
+  constexpr int64_t K = kXcdSkew > 0 ? kXcdSkew : 1, per = 8 * K, tiles_per = per - 4;
+  if (n <= 1) return 1;
+  const int64_t full = (n - 1) / tiles_per, r = (n - 1) % tiles_per;
+  return full * per + (r < (K - 1) * 8 ? r : (K - 1) * 8 + 2 * (r - (K - 1) * 8)) + 1;
+}
+
 struct RedArgs {
   uint64_t in[ZR_MAX_WORLD];   // replica r's flat element f: in[r] + f*sizeof
   uint64_t out[ZR_MAX_WORLD];  // reduce mode: partition d's element j: out[d] + 4j
@@ -374,6 +414,7 @@ struct RedArgs {
   int32_t R;
   float divisor;
   float inv_divisor;
+  int32_t skew;  // 1: one tile per workgroup in the XCD-weighted order (skew_tile)
   // fused mode: the state buffers.  Partition d's element j sits at index
   // d*state_stride + j (state_stride 0: the buffers hold one partition).
   int64_t state_stride;
@@ -549,7 +590,15 @@ __global__ __launch_bounds__((red_threads<InT, kFused>())) ZR_OCCUPANCY void red
   constexpr int64_t kTile = red_tile<InT, kFused>();
   const int rr = R > 0 ? R : a.R;
 
-  for (int64_t t = a.tile_base + blockIdx.x; t < a.tile_end; t += gridDim.x) {
+  int64_t t = a.tile_base + blockIdx.x, tstep = gridDim.x;
+  if constexpr (kXcdSkew > 0) {
+    if (a.skew) {
+      const int64_t j = skew_tile(blockIdx.x);
+      t = j < 0 ? a.tile_end : a.tile_base + j;
+      tstep = a.tile_end;  // one tile per workgroup
+    }
+  }
+  for (; t < a.tile_end; t += tstep) {
     Seg sg;
     if constexpr (kArgSegs)
       sg = a.aseg[find_arg_seg(a.aseg, a.nseg, t)];
@@ -1611,9 +1660,14 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     // A capped grid walks the tiles in steps of its size (the kernel's
     // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
     const int64_t n = as.tile_end - as.tile_base;
+    // Uncapped launches of one tile per workgroup over enough replicas take
+    // the XCD-weighted order.
+    as.skew = kXcdSkew > 0 && max_wgs <= 0 && ZR_GRID_PER_CU == 0 &&
+              gi.world >= ZR_XCD_SKEW_MIN_WORLD;
     const unsigned grid = max_wgs > 0
         ? static_cast<unsigned>(std::min<int64_t>(grid_for(n, cus), max_wgs))
-        : grid_for(n, cus);
+        : as.skew ? static_cast<unsigned>(skew_grid(n))
+                  : grid_for(n, cus);
     if (dt == ZR_BF16)
       st = fused ? launch_reduce_t<uint16_t, true>(as, gi.world, div, dword, argsegs, grid, stream)
                  : launch_reduce_t<uint16_t, false>(as, gi.world, div, dword, argsegs, grid, stream);
