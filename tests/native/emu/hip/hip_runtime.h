@@ -22,6 +22,7 @@
 #define __align__(n) __attribute__((aligned(n)))
 #define HIP_SYMBOL(x) x
 #define ZR_GLOBAL
+#define ZR_CONST
 
 struct zr_emu_dim {
   unsigned x = 0, y = 0, z = 0;

@@ -520,11 +520,25 @@ __device__ __forceinline__ float reduce_one(const RedArgs& a, int rr, int64_t f)
   return acc;
 }
 
-// A value every lane of the wave holds, moved to a scalar register.  Segment
-// tables live in device memory and are read with vector loads; broadcasting
-// the fields tells the compiler they are uniform, so stream bases stay in
-// scalar registers and the slot accesses take a scalar base plus a 32-bit
-// lane offset.
+// Segment tables in device memory are read-only while a kernel runs and
+// every lane of a workgroup reads the same entry, so the kernels read them
+// through the constant address space: scalar loads through the scalar data
+// cache, instead of vector loads that each wait out a full memory round trip
+// under the streams' load (a workgroup makes log2(segments) + 1 dependent
+// table reads before its first stream load).  The tables are written before
+// the launch (host copy or a staging kernel's vector stores); caches are
+// invalidated at kernel start.
+#ifndef ZR_CONST
+#define ZR_CONST __attribute__((address_space(4)))
+#endif
+__device__ __forceinline__ const ZR_CONST Seg* cseg(const Seg* p) {
+  return (const ZR_CONST Seg*)(p);
+}
+
+// A value every lane of the wave holds, moved to a scalar register.
+// Broadcasting the segment fields tells the compiler they are uniform, so
+// stream bases stay in scalar registers and the slot accesses take a scalar
+// base plus a 32-bit lane offset.
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const uint64_t u = static_cast<uint64_t>(x);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
@@ -535,9 +549,9 @@ __device__ __forceinline__ int32_t uniform32(int32_t x) {
   return static_cast<int32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x)));
 }
 __device__ __forceinline__ Seg load_seg(const Seg* p) {
-  const Seg s = *p;
-  return Seg{uniform64(s.flat), uniform64(s.part), uniform64(s.numel),
-             uniform64(s.tile0), uniform32(s.dst), uniform32(s.pad)};
+  const ZR_CONST Seg* c = cseg(p);
+  return Seg{uniform64(c->flat), uniform64(c->part), uniform64(c->numel),
+             uniform64(c->tile0), uniform32(c->dst), uniform32(c->pad)};
 }
 
 // Tile -> segment for a segment array passed in the kernel arguments
@@ -556,10 +570,11 @@ __device__ __forceinline__ int find_arg_seg(const S* segs, int nseg, int64_t t) 
 
 // Tile -> segment by binary search over the segments' first-tile indices.
 __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
+  const ZR_CONST Seg* cs = cseg(segs);
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (uniform64(segs[mid].tile0) <= t) lo = mid; else hi = mid - 1;
+    if (uniform64(cs[mid].tile0) <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
