@@ -35,13 +35,12 @@
  *   - The library owns a plan (create with zr_plan_buckets, free with
  *     zr_plan_free).  A plan is immutable; small device tables derived from
  *     it are built on first use and freed with it.  The first use of a
- *     (group, bucket, dst, device) selection that needs a table allocates it
- *     and uploads it synchronously (one hipMalloc and one hipMemcpy of 48
- *     bytes per segment, typically tens of microseconds); later calls reuse
- *     it.  Reduce selections of at most two segments whose launches span
- *     16K-256K tiles carry their segments in the kernel arguments and need
- *     no table.  A call recorded into a HIP graph must not be the first use
- *     of a selection that needs a table: make it once outside the capture.
+ *     (group, bucket range, dst, device) selection allocates its table and
+ *     uploads it synchronously (one hipMalloc and one hipMemcpy of 40 bytes
+ *     per segment, typically tens of microseconds); later calls reuse it.
+ *     A call recorded into a HIP graph must not be the first use of its
+ *     selection: make it once outside the capture (or use
+ *     zr_reduce_scatter_adam_noalloc, which needs no table).
  *   - Work is enqueued on the caller's HIP stream; nothing synchronises
  *     implicitly.  Completion is the caller's stream synchronisation.  One
  *     call may enqueue several kernel launches: selections whose traffic

@@ -3,8 +3,7 @@
 // Built together with the library's own sources (zr_kernels.hip compiled as
 // C++ with tests/native/emu on the include path, zr_plan.cpp) under
 // AddressSanitizer + UndefinedBehaviorSanitizer, with tiny launch caps so
-// that small cases take the multi-launch, argument-segment and device-table
-// paths.  Random plans, selections (every bucket, one bucket, a bucket
+// that small cases take the multi-launch path.  Random plans, selections (every bucket, one bucket, a bucket
 // range; every destination or one), element types, windows and pointer
 // offsets of 0-3 elements drive every entry point.  Each buffer ends exactly
 // at the end of its allocation (an overrun is an ASan error to the byte);

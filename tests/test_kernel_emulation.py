@@ -3,8 +3,8 @@ UndefinedBehaviorSanitizer: the library's own sources (zr_kernels.hip compiled
 as C++ against tests/native/emu, the planner) driven through the C ABI by
 tests/native/kernel_emu.cpp on random plans, selections, element types,
 windows and pointer offsets, with tiny launch caps so that small cases take
-the multi-launch, argument-segment and device-table paths, and a short
-XCD-weighted tile cycle so that they take its idle slots too.  Any access
+the multi-launch path, and a short XCD-weighted tile cycle so that they take
+its idle slots too.  Any access
 outside a buffer (vector accesses to the byte, scalar ones at ASan's
 granularity), any store before a buffer, and any output that differs from a
 plain loop over the plan's slices fails the run.  The coverage report must
@@ -33,7 +33,6 @@ def _build(tmp_path, kernels_src, name):
     cmd = [CLANG, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-ffp-contract=off",
            "-Wno-align-mismatch", "-D__HIP_PLATFORM_AMD__", "-DZR_LAUNCH_BYTES=65536",
-           "-DZR_ARGSEGS_MIN_TILES=2", "-DZR_ARGSEGS_MAX_TILES=64",
            # an XCD-weighted order of 2-round cycles from 4 replicas up, so
            # that short launches hold whole cycles and both orders run
            "-DZR_XCD_SKEW=2", "-DZR_XCD_SKEW_MIN_WORLD=4",
@@ -49,15 +48,13 @@ def _build(tmp_path, kernels_src, name):
 # Every kernel and variant the random cases must reach (name prefixes as the
 # coverage report prints them).
 REQUIRED = [
-    # fused, common / argument segments / dword-aligned, bf16 and fp32, 8 replicas
-    "reduce_kernel<float, 8, false, true, false, false>",
-    "reduce_kernel<float, 8, false, true, false, true>",
-    "reduce_kernel<float, 8, false, true, true, false>",
-    "reduce_kernel<unsigned short, 8, false, true, false, false>",
-    "reduce_kernel<unsigned short, 8, false, true, false, true>",
-    "reduce_kernel<unsigned short, 8, false, true, true, false>",
+    # fused, common / dword-aligned, bf16 and fp32, 8 replicas
+    "reduce_kernel<float, 8, false, true, false>",
+    "reduce_kernel<float, 8, false, true, true>",
+    "reduce_kernel<unsigned short, 8, false, true, false>",
+    "reduce_kernel<unsigned short, 8, false, true, true>",
     # unfused, run-time replica count, true division
-    "reduce_kernel<float, 8, false, false, false, false>",
+    "reduce_kernel<float, 8, false, false, false>",
     "reduce_kernel<unsigned short, 0, ",
     "reduce_kernel<float, 3, true, ",
     "adam_kernel<true, false>", "adam_kernel<true, true>", "adam_kernel<false, false>",

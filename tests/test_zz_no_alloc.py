@@ -74,8 +74,8 @@ def test_noalloc_equals_allocating_call_twice_second_smaller():
     assert 0 < n2 < n1
 
 
-def test_noalloc_single_bucket_and_argument_segments():
-    # one bucket of a rank's selection, then a selection carried in the
-    # kernel arguments (two segments over 16K+ tiles: nothing staged)
+def test_noalloc_single_bucket_and_large_selection():
+    # one bucket of a rank's selection, then a large two-segment selection
+    # (the last partition's slice and its padding, 8.4M elements)
     _case([70000, 5000, 33], 4, 20000, 2, False, 3, bucket=1)
     _case([4 * 8400000], 4, 1 << 40, 3, True, 4)

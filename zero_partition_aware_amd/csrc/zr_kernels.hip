@@ -426,27 +426,6 @@ struct RedArgs {
   AdamConsts ac;
 };
 
-// RedArgs plus up to kRedArgSegs segments carried in the kernel arguments,
-// for large selections of few segments (the kArgSegs instantiations read
-// their segment from the arguments instead of the device table, which spares
-// every workgroup a dependent global load before its first stream load).
-constexpr int kRedArgSegs = 2;
-// Tile range of the launches that use them (A/B measured: +0.7% on a
-// 108 us launch; slower below ~20 us; no gain to find on 10 ms launches).
-#ifndef ZR_ARGSEGS_MIN_TILES
-#define ZR_ARGSEGS_MIN_TILES 16384
-#endif
-#ifndef ZR_ARGSEGS_MAX_TILES
-#define ZR_ARGSEGS_MAX_TILES 262144
-#endif
-// (The ranges are stated in 512-element tiles and applied as element counts,
-// so they keep their meaning for either tile shape.)
-constexpr int64_t kRedArgSegsMinElems = int64_t(ZR_ARGSEGS_MIN_TILES) * 512;
-constexpr int64_t kRedArgSegsMaxElems = int64_t(ZR_ARGSEGS_MAX_TILES) * 512;
-struct RedArgsS : RedArgs {
-  Seg aseg[kRedArgSegs];
-};
-
 // Segment tables of the no-allocation entry point are staged in a
 // file-scope device array (`scratch`, below) instead of memory the library
 // allocates.  A staging launch copies up to kStageSegs segments from its
@@ -594,9 +573,9 @@ __device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int64_t t) {
 // dword-aligned (vector types with 4-byte alignment).  The host launches that
 // variant only for selections with a segment at which no phase is
 // slot-aligned, so the common instantiations carry none of its code.
-template <typename InT, int R, bool kDiv, bool kFused, bool kDword, bool kArgSegs>
+template <typename InT, int R, bool kDiv, bool kFused, bool kDword>
 __global__ __launch_bounds__((red_threads<InT, kFused>())) ZR_OCCUPANCY void reduce_kernel(
-    const std::conditional_t<kArgSegs, RedArgsS, RedArgs> a) {
+    const RedArgs a) {
   using Vec = typename In<InT>::Vec;
   constexpr int A = kDword ? kDW : 0;  // alignment the slot accesses may assume
   constexpr bool kOddBf16 = kDword && std::is_same_v<InT, uint16_t>;
@@ -614,11 +593,7 @@ __global__ __launch_bounds__((red_threads<InT, kFused>())) ZR_OCCUPANCY void red
     }
   }
   for (; t < a.tile_end; t += tstep) {
-    Seg sg;
-    if constexpr (kArgSegs)
-      sg = a.aseg[find_arg_seg(a.aseg, a.nseg, t)];
-    else
-      sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
+    const Seg sg = load_seg(a.segs + find_seg(a.segs, a.nseg, t));
     const int64_t lt = t - sg.tile0;
     // First element of the segment in the output or state buffers.
     const int64_t spart =
@@ -1449,21 +1424,15 @@ zr_status adam_consts(const zr_adam* h, AdamConsts* k) {
 }
 
 template <typename InT, bool kFused>
-zr_status launch_reduce_t(const RedArgsS& as, int R, bool div, bool dword, bool argsegs,
-                          unsigned grid, hipStream_t st) {
-  const RedArgs& a = as;
-#define ZR_LAUNCH(RR, DD)                                                      \
-  do {                                                                         \
-    constexpr int kTH = red_threads<InT, kFused>();                            \
-    if (dword)                                                                 \
-      ZR_KERNEL_LAUNCH(grid, kTH, st, a,                                       \
-                       reduce_kernel<InT, RR, DD, kFused, true, false>);       \
-    else if (argsegs)                                                          \
-      ZR_KERNEL_LAUNCH(grid, kTH, st, as,                                      \
-                       reduce_kernel<InT, RR, DD, kFused, false, true>);       \
-    else                                                                       \
-      ZR_KERNEL_LAUNCH(grid, kTH, st, a,                                       \
-                       reduce_kernel<InT, RR, DD, kFused, false, false>);      \
+zr_status launch_reduce_t(const RedArgs& a, int R, bool div, bool dword, unsigned grid,
+                          hipStream_t st) {
+#define ZR_LAUNCH(RR, DD)                                                           \
+  do {                                                                              \
+    constexpr int kTH = red_threads<InT, kFused>();                                 \
+    if (dword)                                                                      \
+      ZR_KERNEL_LAUNCH(grid, kTH, st, a, reduce_kernel<InT, RR, DD, kFused, true>); \
+    else                                                                            \
+      ZR_KERNEL_LAUNCH(grid, kTH, st, a, reduce_kernel<InT, RR, DD, kFused, false>);\
   } while (0)
   if (div) {
     switch (R) {
@@ -1649,46 +1618,37 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
       tile * (static_cast<int64_t>(gi.world) * static_cast<int64_t>(s) +
                     (fused ? 26 + (gout ? 4 : 0) : 4));
   const int64_t nl = launches_for(total, tile_bytes);
-  const int64_t per = (total + nl - 1) / nl;
-  // Mid-sized launches over few segments carry their segments in the kernel
-  // arguments (short launches measured faster with the device table); only
-  // the other calls need the device table.
-  const bool argsegs = !dword && nseg <= kRedArgSegs && per * tile >= kRedArgSegsMinElems &&
-                       per * tile <= kRedArgSegsMaxElems;
-  if (!argsegs && noalloc) {
+  if (noalloc) {
     Seg* table = nullptr;
     st = scratch_for(device, &table);
     if (st != ZR_OK) return st;
     st = stage_segments(hs->data(), nseg + 1, table, stream);
     if (st != ZR_OK) return st;
     a.segs = table;
-  } else if (!argsegs) {
+  } else {
     st = get_dev_table(plan, kReduceTable, group, first, last, dst, tile, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
-  RedArgsS as;
-  static_cast<RedArgs&>(as) = a;
-  for (int i = 0; i < kRedArgSegs; ++i) as.aseg[i] = i < nseg ? (*hs)[i] : Seg{};
   for (int64_t i = 0; i < nl; ++i) {
-    as.tile_base = launch_first(total, nl, i);
-    as.tile_end = launch_first(total, nl, i + 1);
+    a.tile_base = launch_first(total, nl, i);
+    a.tile_end = launch_first(total, nl, i + 1);
     // A capped grid walks the tiles in steps of its size (the kernel's
     // grid-stride loop), so the launch holds at most max_wgs workgroup slots.
-    const int64_t n = as.tile_end - as.tile_base;
+    const int64_t n = a.tile_end - a.tile_base;
     // Uncapped launches of one tile per workgroup over enough replicas take
     // the XCD-weighted order.
-    as.skew = kXcdSkew > 0 && max_wgs <= 0 && ZR_GRID_PER_CU == 0 &&
-              gi.world >= ZR_XCD_SKEW_MIN_WORLD;
+    a.skew = kXcdSkew > 0 && max_wgs <= 0 && ZR_GRID_PER_CU == 0 &&
+             gi.world >= ZR_XCD_SKEW_MIN_WORLD;
     const unsigned grid = max_wgs > 0
         ? static_cast<unsigned>(std::min<int64_t>(grid_for(n, cus), max_wgs))
-        : as.skew ? static_cast<unsigned>(skew_grid(n))
-                  : grid_for(n, cus);
+        : a.skew ? static_cast<unsigned>(skew_grid(n))
+                 : grid_for(n, cus);
     if (dt == ZR_BF16)
-      st = fused ? launch_reduce_t<uint16_t, true>(as, gi.world, div, dword, argsegs, grid, stream)
-                 : launch_reduce_t<uint16_t, false>(as, gi.world, div, dword, argsegs, grid, stream);
+      st = fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, dword, grid, stream)
+                 : launch_reduce_t<uint16_t, false>(a, gi.world, div, dword, grid, stream);
     else
-      st = fused ? launch_reduce_t<float, true>(as, gi.world, div, dword, argsegs, grid, stream)
-                 : launch_reduce_t<float, false>(as, gi.world, div, dword, argsegs, grid, stream);
+      st = fused ? launch_reduce_t<float, true>(a, gi.world, div, dword, grid, stream)
+                 : launch_reduce_t<float, false>(a, gi.world, div, dword, grid, stream);
     if (st != ZR_OK) return st;
   }
   return ZR_OK;
