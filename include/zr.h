@@ -346,8 +346,7 @@ zr_status zr_reduce_scatter_adam_capped(const zr_plan* plan, int32_t group,
  * that the library holds on each GPU for the life of the process: at most
  * 6,552 segments per selection, else ZR_ERR_INVALID before anything is
  * enqueued.  (A selection's segments are its merged slices plus one padding
- * segment per selected partition; selections of at most two segments whose
- * launches span 16K-256K tiles need no table at all.)  Every call on one GPU
+ * segment per selected partition that holds padding.)  Every call on one GPU
  * shares that GPU's array and leaves its own table there, so calls that
  * overlap on one GPU -- on different streams without an ordering between
  * them -- race: order them on one stream or with events.  The plan's
