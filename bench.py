@@ -719,18 +719,26 @@ def setup_llama(torch, zr, workloads, ipg=False):
                 vs.append(b[a:a + w.numels[p]])
                 a += w.numels[p]
             views.append(vs)
-        bytes_per_step = w.micro_batches * R * 10 * P
+        # The first micro-batch writes the window it would have added into
+        # after the step's zeroing (6 B per element: bf16 read, fp32
+        # written); the others add into it (10 B: bf16 read, fp32 read and
+        # written).
+        bytes_per_step = R * P * (6 + 10 * (w.micro_batches - 1))
 
         def step(i, timer):
-            for mu in range(w.micro_batches):
+            for r in range(R):
+                timer.launch(lambda: zr.zr_ipg_accumulate_first(plan, pids, views[r], mgs[r],
+                                                                window_base=lo), "ipg_first")
+            for mu in range(1, w.micro_batches):
                 for r in range(R):
                     timer.launch(lambda: zr.zr_ipg_accumulate(plan, pids, views[r], mgs[r],
                                                               window_base=lo), "ipg")
 
         cfg.update(micro_batches=w.micro_batches, grad_dtype="bf16 -> fp32 main_grad",
+                   first_micro_batch="zr_ipg_accumulate_first (main_grad not read)",
                    bytes_per_step=bytes_per_step)
         return step, bytes_per_step, P * w.micro_batches * R, cfg, \
-            {"ipg": 10 * P}, "ipg", None
+            {"ipg_first": 6 * P, "ipg": 10 * P}, "ipg", None
 
     master = workloads.device_normal(workloads.seed_for(name, k, master=True), P,
                                       w.master_sigma, "cuda")

@@ -223,6 +223,22 @@ zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param_ids,
                             int64_t window_base, int64_t window_len,
                             hipStream_t stream);
 
+/* zr_ipg_accumulate_first -- the first micro-batch of a step: what
+ * zr_ipg_accumulate gives on a main_grad window zeroed at the start of the
+ * step, without the zeroing and without reading main_grad ([Megatron DP]
+ * "深入：朴素 DP 的 all-reduce" step 2: the fp32 buffer is zeroed each step
+ * and each micro-batch's gradient is added into it).  Same arguments and
+ * errors as zr_ipg_accumulate.  Per element of each listed param (clipped to
+ * the window): main_grad[f - window_base] = fl(+0 + widen(grad)), the bits
+ * the add into +0 gives (a -0 gradient gives +0).  Elements of the window no
+ * listed param covers are not written.  Later micro-batches use
+ * zr_ipg_accumulate.  It moves s + 4 bytes per element instead of s + 8. */
+zr_status zr_ipg_accumulate_first(const zr_plan* plan, const int64_t* param_ids,
+                                  const void* const* grads, int64_t n,
+                                  zr_dtype grad_dtype, float* main_grad,
+                                  int64_t window_base, int64_t window_len,
+                                  hipStream_t stream);
+
 /* zr_reduce_scatter_local -- the partition-aware reduction with its copy
  * into the local partition ([ZeRO-RS blog §三.2, §三.3, §六];
  * [Megatron DP] step 4; [Collectives] ReduceScatter definition).

@@ -373,10 +373,13 @@ void ipg_case(Rng& r, int seed) {
     if (pl.pg[p] == g && r.uni(0, 3) != 0) ids.push_back(static_cast<int64_t>(p));
   if (ids.empty() || gi.L == 0) return;
   const bool bf16 = r.uni(0, 1) == 1;
+  // the step's first micro-batch: main_grad taken as +0 and not read
+  const bool first = r.uni(0, 2) == 0;
   const int64_t wb = r.uni(0, gi.L - 1), wl = r.uni(0, gi.L - wb);
   Buf mg(static_cast<size_t>(std::max<int64_t>(wl, 1)), 4, off(r));
   std::vector<float> want(wl);
   for (int64_t i = 0; i < wl; ++i) { want[i] = r.normal(1.0f); mg.f()[i] = want[i]; }
+  std::vector<char> touched(static_cast<size_t>(wl), 0);
   std::vector<Buf*> gs;
   std::vector<const void*> ptrs;
   for (int64_t p : ids) {
@@ -389,13 +392,20 @@ void ipg_case(Rng& r, int seed) {
       if (bf16) { b->h()[i] = bf16_of(x); w = bits_f(static_cast<uint32_t>(b->h()[i]) << 16); }
       else b->f()[i] = x;
       const int64_t f = off + i;
-      if (f >= wb && f < wb + wl) want[f - wb] = want[f - wb] + w;
+      if (f >= wb && f < wb + wl) {
+        // +0 + w, not w: a -0 gradient gives +0 into a zeroed buffer
+        if (first && !touched[f - wb]) want[f - wb] = 0.0f;
+        touched[f - wb] = 1;
+        want[f - wb] = want[f - wb] + w;
+      }
     }
     gs.push_back(b);
     ptrs.push_back(b->p);
   }
-  const zr_status st = zr_ipg_accumulate(pl.h, ids.data(), ptrs.data(), static_cast<int64_t>(ids.size()),
-                                         bf16 ? ZR_BF16 : ZR_FP32, mg.f(), wb, wl, nullptr);
+  const zr_status st =
+      (first ? zr_ipg_accumulate_first : zr_ipg_accumulate)(
+          pl.h, ids.data(), ptrs.data(), static_cast<int64_t>(ids.size()),
+          bf16 ? ZR_BF16 : ZR_FP32, mg.f(), wb, wl, nullptr);
   CHECK(st == ZR_OK, "seed %d: ipg failed: %s", seed, zr_last_error());
   for (int64_t i = 0; i < wl; ++i)
     CHECK(f_bits(mg.f()[i]) == f_bits(want[i]), "seed %d: main_grad [%lld]", seed, (long long)i);

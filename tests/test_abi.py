@@ -180,17 +180,19 @@ def test_prepared_call_checks_its_arguments_once():
         zr.prepare_reduce_scatter_adam(plan, 0, 0, reps, buf, buf, buf)(-1, 0, stream=0)
 
 
-def test_ipg_rejects_mixed_groups_duplicates_and_overrun():
+@pytest.mark.parametrize("first", [False, True])
+def test_ipg_rejects_mixed_groups_duplicates_and_overrun(first):
+    ipg = zr.zr_ipg_accumulate_first if first else zr.zr_ipg_accumulate
     plan = zr.zr_plan_buckets([10, 20, 30], [0, 1, 0], [(2, 1), (2, 1)], 16)
     g = _FakeTensor(0x1000, 10, "bf16")
     g20 = _FakeTensor(0x2000, 20, "bf16")
     mg = _FakeTensor(0x100000, 40)
     with pytest.raises(zr.ZrError, match="share a group"):
-        zr.zr_ipg_accumulate(plan, [0, 1], [g, g20], mg, stream=0)
+        ipg(plan, [0, 1], [g, g20], mg, stream=0)
     with pytest.raises(zr.ZrError, match="twice"):
-        zr.zr_ipg_accumulate(plan, [0, 0], [g, g], mg, stream=0)
+        ipg(plan, [0, 0], [g, g], mg, stream=0)
     with pytest.raises(zr.ZrError, match="past"):
-        zr.zr_ipg_accumulate(plan, [0], [g], mg, window_base=1, window_len=40, stream=0)
+        ipg(plan, [0], [g], mg, window_base=1, window_len=40, stream=0)
 
 
 def test_ipg_rejects_gradient_smaller_than_its_param():

@@ -618,3 +618,57 @@ def test_dword_phases_runtime_replica_count(R):
         assert_within(host_f32(dm), w_m, what=f"rank {k} m")
         assert_within(host_f32(dv), w_v, atol=0.0, what=f"rank {k} v")
         assert np.array_equal(host_u16(pb), bf16_rne_oracle(got)), f"rank {k} bf16"
+
+
+@pytest.mark.parametrize("is_bf16", [True, False])
+def test_ipg_first_micro_batch_equals_add_into_zeros(is_bf16):
+    """zr_ipg_accumulate_first (the step's first micro-batch, main_grad not
+    read) against zr_ipg_accumulate into a zeroed window and the oracle's IPG
+    from zeros, bit for bit: -0 and special values among the gradients,
+    windows clipping params at both ends, gradient and main_grad pointers off
+    by 0-3 elements (the dword-aligned variant included); elements no listed
+    param covers keep what the window held; later micro-batches accumulate
+    onto the first one's result."""
+    rng = np.random.default_rng(21 + int(is_bf16))
+    numels = [4096 * 3 + 5, 1, 700, 33, 20000, 6]
+    n = len(numels)
+    plan = zr.zr_plan_buckets(numels, [0] * n, [(2, 1)], 1 << 30)
+    ref = plan_oracle(numels, [0] * n, [(2, 1)], 1 << 30)
+    total = ref.groups[0].padded
+    listed = [0, 2, 3, 4]                       # params 1 and 5 are not listed
+    specials = np.array([-0.0, 0.0, np.inf, -np.inf, np.nan, 1e-40, -1e-40, 3e38],
+                        np.float32)
+    for base, length, off_g, off_mg in [(0, total, 0, 0), (7, 15000, 1, 3),
+                                        (12290, total - 12290 - 3, 2, 1)]:
+        grads = []
+        for p in listed:
+            x = (rng.standard_normal(numels[p]) * 1e-3).astype(np.float32)
+            x[: min(len(specials), numels[p])] = specials[: min(len(specials), numels[p])]
+            if is_bf16:
+                x = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            grads.append(x)
+        fill = rng.standard_normal(length).astype(np.float32)
+        got = to_dev(fill, off_mg)
+        zr.zr_ipg_accumulate_first(plan, listed, [to_dev(x, off_g) for x in grads], got,
+                                   window_base=base)
+        zeros = to_dev(np.zeros(length, np.float32), off_mg)
+        zr.zr_ipg_accumulate(plan, listed, [to_dev(x, off_g) for x in grads], zeros,
+                             window_base=base)
+        want = np.zeros(length, np.float32)
+        ipg_accumulate_oracle(want, base, ref.param_offset, listed, grads, is_bf16)
+        covered = np.zeros(length, bool)
+        for p in listed:
+            lo = max(ref.param_offset[p], base) - base
+            hi = min(ref.param_offset[p] + numels[p], base + length) - base
+            if hi > lo:
+                covered[lo:hi] = True
+        g = host_f32(got)
+        assert_bits_equal(g[covered], want[covered], "first micro-batch vs oracle")
+        assert_bits_equal(g[covered], host_f32(zeros)[covered], "first vs add into zeros")
+        assert_bits_equal(g[~covered], fill[~covered], "elements no listed param covers")
+        # a second micro-batch accumulates onto the first one's result
+        grads2 = [_draw(rng, numels[p], is_bf16) for p in listed]
+        zr.zr_ipg_accumulate(plan, listed, [to_dev(x, off_g) for x in grads2], got,
+                             window_base=base)
+        ipg_accumulate_oracle(want, base, ref.param_offset, listed, grads2, is_bf16)
+        assert_bits_equal(host_f32(got)[covered], want[covered], "second micro-batch")

@@ -58,8 +58,10 @@ REQUIRED = [
     "reduce_kernel<unsigned short, 0, ",
     "reduce_kernel<float, 3, true, ",
     "adam_kernel<true, false>", "adam_kernel<true, true>", "adam_kernel<false, false>",
-    "ipg_kernel<float, false>", "ipg_kernel<float, true>",
-    "ipg_kernel<unsigned short, false>", "ipg_kernel<unsigned short, true>",
+    "ipg_kernel<float, false, false>", "ipg_kernel<float, true, false>",
+    "ipg_kernel<unsigned short, false, false>", "ipg_kernel<unsigned short, true, false>",
+    "ipg_kernel<float, false, true>", "ipg_kernel<float, true, true>",
+    "ipg_kernel<unsigned short, false, true>", "ipg_kernel<unsigned short, true, true>",
     "copy_kernel<false>", "copy_kernel<true>",
     "gather_kernel<float, false>", "gather_kernel<float, true>",
     "gather_kernel<unsigned short, false>", "gather_kernel<unsigned short, true>",

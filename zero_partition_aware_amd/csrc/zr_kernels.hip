@@ -876,7 +876,10 @@ struct IpgArgs {
 // that puts main_grad on 16 bytes (there always is one) and read the
 // gradient dword-aligned -- or, for bf16 an odd number of elements off, with
 // ld_bf16_odd.  The host launches that variant only for calls that need it.
-template <typename InT, bool kDword>
+// kFirst: the step's first micro-batch into a window the step would have
+// zeroed: main_grad is not read, and each element becomes fl(+0 + widen(g)),
+// the bits the add into a zeroed buffer gives (-0 becomes +0).
+template <typename InT, bool kDword, bool kFirst>
 __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
   using Vec = typename In<InT>::Vec;
   constexpr int A = kDword ? kDW : 0;  // alignment the gradient reads may assume
@@ -920,7 +923,10 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
         } else {
           x[u] = ld_stream<Vec, A>(reinterpret_cast<const void*>(sg.src + rel * sizeof(InT)));
         }
-        cur[u] = ld_stream<f32x4>(a.main_grad + sg.dst + rel);
+        if constexpr (kFirst)
+          cur[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        else
+          cur[u] = ld_stream<f32x4>(a.main_grad + sg.dst + rel);
       }
     }
 #pragma unroll
@@ -937,7 +943,8 @@ __global__ __launch_bounds__(kThreads) void ipg_kernel(const IpgArgs a) {
         const int64_t e1 = rel + VE < sg.numel ? rel + VE : sg.numel;
         for (int64_t e = e0; e < e1; ++e) {
           const float v = In<InT>::widen(*reinterpret_cast<const InT*>(sg.src + e * sizeof(InT)));
-          a.main_grad[sg.dst + e] = a.main_grad[sg.dst + e] + v;
+          const float c = kFirst ? 0.0f : a.main_grad[sg.dst + e];
+          a.main_grad[sg.dst + e] = c + v;
         }
       }
     }
@@ -1814,11 +1821,24 @@ extern "C" zr_status zr_adam_partition(const zr_adam* h, const float* grad, floa
   return ZR_OK;
 }
 
-extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param_ids,
-                                       const void* const* grads, int64_t n,
-                                       zr_dtype grad_dtype, float* main_grad,
-                                       int64_t window_base, int64_t window_len,
-                                       hipStream_t stream) {
+namespace {
+template <bool kFirst>
+void launch_ipg(const IpgArgs& a, zr_dtype grad_dtype, bool dword, unsigned grid,
+                hipStream_t stream) {
+  if (grad_dtype == ZR_BF16) {
+    if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, true, kFirst>);
+    else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, false, kFirst>);
+  } else {
+    if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, true, kFirst>);
+    else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, false, kFirst>);
+  }
+}
+
+// Validation and launches of both IPG entry points; `first`: main_grad is
+// taken as zero and not read.
+zr_status run_ipg(const zr_plan* plan, const int64_t* param_ids, const void* const* grads,
+                  int64_t n, zr_dtype grad_dtype, float* main_grad, int64_t window_base,
+                  int64_t window_len, bool first, hipStream_t stream) {
   zr::clear_error();
   try {
     if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
@@ -1881,18 +1901,17 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
                 aligned(mgp + static_cast<uint64_t>(a.seg[i].dst + j) * 4, 16);
         dword = !any;
       }
-      const int64_t nl = launches_for(tiles, kIpgTileElems * static_cast<int64_t>(s + 8));
+      // Bytes per tile: the gradient read, main_grad written (and read).
+      const int64_t nl =
+          launches_for(tiles, kIpgTileElems * static_cast<int64_t>(s + (first ? 4 : 8)));
       for (int64_t i = 0; i < nl; ++i) {
         a.tile_base = launch_first(tiles, nl, i);
         a.tile_end = launch_first(tiles, nl, i + 1);
         const unsigned grid = grid_for(a.tile_end - a.tile_base, cus);
-        if (grad_dtype == ZR_BF16) {
-          if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, true>);
-          else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<uint16_t, false>);
-        } else {
-          if (dword) ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, true>);
-          else ZR_KERNEL_LAUNCH(grid, kThreads, stream, a, ipg_kernel<float, false>);
-        }
+        if (first)
+          launch_ipg<true>(a, grad_dtype, dword, grid, stream);
+        else
+          launch_ipg<false>(a, grad_dtype, dword, grid, stream);
         st = check_launch("ipg_accumulate launch");
         if (st != ZR_OK) return st;
       }
@@ -1901,6 +1920,25 @@ extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
+}
+}  // namespace
+
+extern "C" zr_status zr_ipg_accumulate(const zr_plan* plan, const int64_t* param_ids,
+                                       const void* const* grads, int64_t n,
+                                       zr_dtype grad_dtype, float* main_grad,
+                                       int64_t window_base, int64_t window_len,
+                                       hipStream_t stream) {
+  return run_ipg(plan, param_ids, grads, n, grad_dtype, main_grad, window_base, window_len,
+                 false, stream);
+}
+
+extern "C" zr_status zr_ipg_accumulate_first(const zr_plan* plan, const int64_t* param_ids,
+                                             const void* const* grads, int64_t n,
+                                             zr_dtype grad_dtype, float* main_grad,
+                                             int64_t window_base, int64_t window_len,
+                                             hipStream_t stream) {
+  return run_ipg(plan, param_ids, grads, n, grad_dtype, main_grad, window_base, window_len,
+                 true, stream);
 }
 
 extern "C" zr_status zr_copy_grads_in_partition(const zr_plan* plan, int32_t group,

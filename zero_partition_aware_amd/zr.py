@@ -96,6 +96,8 @@ _sigs = {
     "zr_plan_param_buckets": (c_i32, [c_vp, c_i64, _P(c_i64), _P(c_i64)]),
     "zr_ipg_accumulate": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
                                   c_i64, c_i64, c_vp]),
+    "zr_ipg_accumulate_first": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
+                                        c_i64, c_i64, c_vp]),
     "zr_reduce_scatter_local": (c_i32, [c_vp, c_i32, c_i64, c_i32, _P(zr_replica),
                                         c_i32, _P(c_vp), c_vp]),
     "zr_reduce_scatter_local_range": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32,
@@ -383,6 +385,19 @@ def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
                       window_len=None, stream=None):
     """grads[i]: tensor of param param_ids[i] (bf16 or fp32, all one dtype);
     main_grad: fp32 window tensor."""
+    _ipg(_lib.zr_ipg_accumulate, plan, param_ids, grads, main_grad, window_base, window_len,
+         stream)
+
+
+def zr_ipg_accumulate_first(plan, param_ids, grads, main_grad, window_base=0,
+                            window_len=None, stream=None):
+    """The step's first micro-batch: as zr_ipg_accumulate on a zeroed window,
+    without reading (or zeroing) main_grad."""
+    _ipg(_lib.zr_ipg_accumulate_first, plan, param_ids, grads, main_grad, window_base,
+         window_len, stream)
+
+
+def _ipg(fn, plan, param_ids, grads, main_grad, window_base, window_len, stream):
     n = len(param_ids)
     if len(grads) != n:
         raise ZrError(ZR_ERR_INVALID, "param_ids and grads differ in length")
@@ -397,9 +412,8 @@ def zr_ipg_accumulate(plan, param_ids, grads, main_grad, window_base=0,
     ptrs = (c_vp * max(n, 1))(*[_buf(g, f"grads[{i}]", dt, need(i)).value
                                 for i, g in enumerate(grads)])
     wl = main_grad.numel() if window_len is None else _i64(window_len, "window_len")
-    _check(_lib.zr_ipg_accumulate(plan.handle, ids, ptrs, n, dt,
-                                  _buf(main_grad, "main_grad", ZR_FP32, wl),
-                                  _i64(window_base, "window_base"), wl, _stream(stream)))
+    _check(fn(plan.handle, ids, ptrs, n, dt, _buf(main_grad, "main_grad", ZR_FP32, wl),
+              _i64(window_base, "window_base"), wl, _stream(stream)))
 
 
 def _replicas(reps, plan, group):
