@@ -221,15 +221,21 @@ def test_llama3_8b_ipg_then_fused_rank_windows():
         offs = np.array([ref.param_offset[p] for p in pids], dtype=np.int64)
         which = np.searchsorted(offs, flat, side="right") - 1
         pos = starts[which] + (flat - offs[which])
-        mgs = [torch.zeros(P, device=DEV) for _ in range(R)]
+        # rank 0 accumulates every micro-batch into zeroed windows; the last
+        # rank writes its first micro-batch with zr_ipg_accumulate_first into
+        # windows that hold NaN (never read), then accumulates the others
+        first = k == R - 1
+        mgs = [torch.full((P,), float("nan"), device=DEV) if first else torch.zeros(P, device=DEV)
+               for _ in range(R)]
         mg_s = [np.zeros(idx.size, np.float32) for _ in range(R)]
         gbuf = torch.empty(buf_n, dtype=torch.bfloat16, device=DEV)
         views = [gbuf[int(starts[i]):int(starts[i + 1])] for i in range(len(pids))]
         for mu in range(w.micro_batches):
+            ipg = zr.zr_ipg_accumulate_first if first and mu == 0 else zr.zr_ipg_accumulate
             for r in range(R):
                 workloads.device_normal(workloads.seed_for(name, r, mu), buf_n,
                                         w.grad_sigma, DEV, "bf16", out=gbuf)
-                zr.zr_ipg_accumulate(plan, pids, views, mgs[r], window_base=lo)
+                ipg(plan, pids, views, mgs[r], window_base=lo)
                 gs = _gather(gbuf, pos)
                 # oracle on the samples: one add per micro-batch, in order
                 ipg_accumulate_oracle(mg_s[r], 0, [0], [0], [gs], True)
