@@ -63,6 +63,14 @@ def traffic_for(kernel_key):
     return entry.get("hbm_bytes_per_call")
 
 
+def reduce_dispatches(zr, plan, group, dst, grad_dtype, fused):
+    """Kernel launches one reduce call over every bucket makes (the library's
+    own launch-shape query), so a call's event-timed average can be set
+    beside a profiler's per-dispatch average."""
+    nb = zr.zr_plan_num_buckets(plan)
+    return zr.zr_plan_reduce_launches(plan, group, 0, nb, dst, grad_dtype, fused)[1]
+
+
 # Calls actually made per label over the whole run (every timer), reported
 # by single-workload runs so counter totals can be divided per call.
 CALLS = {}
@@ -278,6 +286,7 @@ def setup_gpt2(torch, zr, workloads, all_ranks=False):
         return combine_checks(out)
 
     step.parity = parity
+    step.dispatches = {"fused": reduce_dispatches(zr, plan, 0, 0, "bf16", True)}
 
     cfg = {"workload": name, "params": len(w.numels), "total_elems": T,
            "replicas": R, "grad_dtype": "bf16", "reduce_bucket_size": w.reduce_bucket_size,
@@ -306,8 +315,9 @@ def setup_gpt2(torch, zr, workloads, all_ranks=False):
             timer.launch(lambda: zr.zr_reduce_scatter_adam(
                 plan, 0, -1, -1, reps, master, m, v, pbf16, None, step=i + 1, **HP), "fused")
 
+        step_all.dispatches = {"fused": reduce_dispatches(zr, plan, 0, -1, "bf16", True)}
         cfg.update(workload=name + "-all-ranks", bytes_per_step=R * bytes_per_step,
-                   share="all 8 ranks' partitions in one fused launch per step")
+                   share="all 8 ranks' partitions in one fused call per step")
         return step_all, R * bytes_per_step, R * P, cfg, {"fused": R * bytes_per_step}, \
             "fused", None
     return step, bytes_per_step, P, cfg, launch_bytes, "fused", cpu_leg
@@ -765,6 +775,7 @@ def setup_llama(torch, zr, workloads, ipg=False):
                                                       gout, step=t, **HP))})
 
     step.parity = parity
+    step.dispatches = {"fused": reduce_dispatches(zr, plan, 0, k, "fp32", True)}
     cfg.update(grad_dtype="fp32 main_grad", bytes_per_step=bytes_per_step)
     def cpu_leg():
         return cpu_oracle_chunk(torch, mgs, master, P, R, D, 1 << 26)
@@ -826,6 +837,8 @@ def setup_moe(torch, zr, workloads):
         return combine_checks(out)
 
     step.parity = parity
+    step.dispatches = {f"fused_g{g}": reduce_dispatches(zr, plan, g, 0, "fp32", True)
+                       for g in range(len(groups))}
 
     cfg = {"workload": name, "params": len(w.numels), "groups": w.groups,
            "reduce_bucket_size": w.reduce_bucket_size,
@@ -1164,6 +1177,12 @@ def measure(torch, zr, workloads, setup, steps, warmup, workload, cpu=True, chec
             "kernel": dominant, "avg_launch_us": round(dom["avg_us"], 2),
             "median_launch_us_event_per_launch": dom["median_us_event_per_launch"],
             "algorithmic_bytes_per_launch": launch_bytes[dominant]}
+    # A call may be several equal kernel launches (calls over ~2 GiB are cut):
+    # the per-dispatch average is what a kernel trace reports.
+    dpc = getattr(step, "dispatches", {}).get(dominant)
+    if dpc:
+        roof["dispatches_per_call"] = dpc
+        roof["avg_dispatch_us"] = round(dom["avg_us"] / dpc, 2)
     out = {"value": round(bytes_per_step / wall_step_s / 1e9, 1), "unit": "GB/s",
            "steps": steps, "warmup": warmup, "ms_per_step": round(1e3 * wall_step_s, 4),
            "config": cfg,

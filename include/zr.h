@@ -202,6 +202,25 @@ zr_status zr_plan_param_buckets(const zr_plan* plan, int64_t p, int64_t* first,
 zr_status zr_plan_slices(const zr_plan* plan, int64_t bucket,
                          const zr_slice** s, int64_t* n);
 
+/* The launch shape of a reduce call, without making it (host only; no GPU
+ * needed): the tiles of the selection -- `group`, the buckets [bucket_first,
+ * bucket_first + bucket_count), destination `dst` (-1 = every destination)
+ * -- and the kernel launches zr_reduce_scatter_local_range (fused = 0) or
+ * zr_reduce_scatter_adam_range (fused = 1, with_grad_out = whether grad_out
+ * is given) cut it into, for grad_dtype replicas.  The same selection
+ * through the one-bucket calls has the same shape.  A call over a selection
+ * that moves more than about 2 GiB makes several equal launches on its
+ * stream; a capped call makes as many.  *tiles and *launches are 0 for a
+ * selection with no slices.  Either output pointer may be null, not both.
+ * Errors: ZR_ERR_INVALID for a bad group, range, dst or dtype.
+ * ([ZeRO-RS blog §三.2]: the selection is the merged slices of the bucket
+ * range bound for `dst`.) */
+zr_status zr_plan_reduce_launches(const zr_plan* plan, int32_t group,
+                                  int64_t bucket_first, int64_t bucket_count,
+                                  int32_t dst, zr_dtype grad_dtype, int32_t fused,
+                                  int32_t with_grad_out, int64_t* tiles,
+                                  int64_t* launches);
+
 /* ------------------------------------------------------------- kernels --- */
 
 /* zr_ipg_accumulate -- add each listed param's gradient into the contiguous

@@ -371,3 +371,52 @@ def test_binding_handles_a_group_without_params():
     zr.zr_reduce_scatter_local(plan, 1, -1, 0, reps, [_FakeTensor(0x100000, 0)], stream=0)
     with pytest.raises(zr.ZrError, match="reps has 3 entries; the call needs 4"):
         zr.zr_reduce_scatter_local(plan, 1, -1, 0, reps[:3], [_FakeTensor(0x100000, 0)], stream=0)
+
+
+def test_reduce_launch_shape_follows_the_stated_rules():
+    """zr_plan_reduce_launches against the launch rules the header states,
+    worked out from the oracle plan: a tile is 512 elements for the bf16
+    fused step and 256 otherwise, a segment of n elements spans
+    (n + 63 + tile - 1) // tile tiles (padding included), and a selection is
+    cut into ceil(tiles / floor(2^31 / tile bytes)) equal launches."""
+    from oracle.plan import plan_oracle
+
+    def rule(ref, g, first, last, dst, bf16, fused, gout):
+        info = ref.groups[g]
+        tile = 512 if bf16 and fused else 256
+        segs = [s.numel for s in ref.slices
+                if s.group == g and first <= s.bucket < last and (dst < 0 or s.dst == dst)]
+        if last == ref.num_buckets:
+            for d in ([dst] if dst >= 0 else range(info.world)):
+                pad = max(0, min(info.part_numel, (d + 1) * info.part_numel - info.total))
+                if pad:
+                    segs.append(pad)
+        tiles = sum((n + 63 + tile - 1) // tile for n in segs)
+        tb = tile * (info.world * (2 if bf16 else 4) + ((26 + (4 if gout else 0)) if fused else 4))
+        per = (2 ** 31) // tb
+        return tiles, (-(-tiles // per) if tiles else 0)
+
+    cases = [([37, 64 * 33, 129], [0, 0, 0], [(4, 1)], 1000),
+             ([8 * 40_000_000 - 10], [0], [(8, 1)], 290_000_000),
+             ([36_000_000], [0], [(4, 1)], 13_500_000),
+             ([300_000, 5, 70_000, 1_234_567], [0, 1, 0, 1], [(8, 2), (2, 2)], 100_000)]
+    for numels, pg, groups, B in cases:
+        ref = plan_oracle(numels, pg, groups, B)
+        plan = zr.zr_plan_buckets(numels, pg, groups, B)
+        nb = ref.num_buckets
+        for g in range(len(groups)):
+            for dst in [-1] + list(range(groups[g][0])):
+                for first, last in [(0, nb), (0, 1), (nb - 1, nb), (nb // 2, nb)]:
+                    for bf16 in (False, True):
+                        for fused, gout in ((False, False), (True, False), (True, True)):
+                            got = zr.zr_plan_reduce_launches(
+                                plan, g, first, last - first, dst, "bf16" if bf16 else "fp32",
+                                fused, gout)
+                            assert got == rule(ref, g, first, last, dst, bf16, fused, gout), \
+                                (numels, g, dst, first, last, bf16, fused, gout)
+    with pytest.raises(zr.ZrError):
+        zr.zr_plan_reduce_launches(plan, 0, 0, nb + 1, 0, "fp32", True)
+    with pytest.raises(zr.ZrError):
+        zr.zr_plan_reduce_launches(plan, 0, 0, 1, 99, "fp32", True)
+    with pytest.raises(zr.ZrError):
+        zr.zr_plan_reduce_launches(plan, 0, 0, 1, 0, "fp16", True)

@@ -66,6 +66,10 @@ def _run(numels, R, B, dst, is_bf16, fused, seed, expect_segs, expect_launches):
     tile_bytes = tile * (R * s_in + (30 if fused else 4))
     nl, _ = _launch_split(tiles, tile_bytes)
     assert nl == expect_launches
+    # the library's own launch-shape query agrees (fused calls here write grad_out)
+    nb = zr.zr_plan_num_buckets(plan)
+    assert zr.zr_plan_reduce_launches(plan, 0, 0, nb, dst, "bf16" if is_bf16 else "fp32",
+                                      fused, fused) == (tiles, nl)
     # replica windows of partition dst, drawn on the device from seeds
     lo, n_real = dst * P, min(P, max(0, T - dst * P))
     dt = "bf16" if is_bf16 else "fp32"

@@ -1505,6 +1505,20 @@ zr_status stage_segments(const Seg* segs, int64_t n, Seg* table, hipStream_t str
 // Shared validation + launch of the reduce kernel in either mode; max_wgs > 0
 // caps the grid (0: one workgroup per tile).  noalloc: the segment table is
 // staged in `scratch` instead of the plan's device table.
+// Tile shape of a reduce call's kernels, by replica element type and kernel.
+int64_t reduce_tile(zr_dtype dt, bool fused) {
+  return dt != ZR_BF16 ? red_tile<float, true>()
+         : fused       ? red_tile<uint16_t, true>()
+                       : red_tile<uint16_t, false>();
+}
+// Bytes one tile of a reduce call moves (the replicas, plus the partition
+// output or the Adam state), which sets how many launches a selection is cut
+// into.
+int64_t reduce_tile_bytes(int64_t tile, int world, size_t s, bool fused, bool gout) {
+  return tile * (static_cast<int64_t>(world) * static_cast<int64_t>(s) +
+                 (fused ? 26 + (gout ? 4 : 0) : 4));
+}
+
 zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t last,
                      int32_t dst,
                      const zr_replica* reps, zr_dtype dt, float* const* part_out,
@@ -1557,10 +1571,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     }
   }
   const std::vector<Seg>* hs = nullptr;
-  // Tile shape of this call's kernels (by replica element type and kernel).
-  const int64_t tile = dt != ZR_BF16 ? red_tile<float, true>()
-                       : fused       ? red_tile<uint16_t, true>()
-                                     : red_tile<uint16_t, false>();
+  const int64_t tile = reduce_tile(dt, fused);
   zr_status st = get_host_table(plan, kReduceTable, group, first, last, dst, tile, &hs);
   if (st != ZR_OK) return st;
   const int nseg = static_cast<int>(hs->size()) - 1;
@@ -1619,12 +1630,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
   };
   bool dword = false;
   for (int i = 0; i < nseg && !dword; ++i) dword = !slot_phase_exists((*hs)[i]);
-  // Bytes one tile moves (the replicas, plus the partition output or the
-  // Adam state), which sets how many launches the selection is cut into.
-  const int64_t tile_bytes =
-      tile * (static_cast<int64_t>(gi.world) * static_cast<int64_t>(s) +
-                    (fused ? 26 + (gout ? 4 : 0) : 4));
-  const int64_t nl = launches_for(total, tile_bytes);
+  const int64_t nl = launches_for(total, reduce_tile_bytes(tile, gi.world, s, fused, gout));
   if (noalloc) {
     Seg* table = nullptr;
     st = scratch_for(device, &table);
@@ -1682,6 +1688,42 @@ std::pair<int64_t, int64_t> count_range(const zr_plan* plan, int64_t first, int6
   return {first, first + count};
 }
 }  // namespace
+
+extern "C" zr_status zr_plan_reduce_launches(const zr_plan* plan, int32_t group,
+                                             int64_t bucket_first, int64_t bucket_count,
+                                             int32_t dst, zr_dtype grad_dtype, int32_t fused,
+                                             int32_t with_grad_out, int64_t* tiles,
+                                             int64_t* launches) {
+  zr::clear_error();
+  try {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is null");
+    if (group < 0 || group >= static_cast<int32_t>(plan->groups.size()))
+      return fail(ZR_ERR_INVALID, "group index out of range");
+    const auto fl = count_range(plan, bucket_first, bucket_count);
+    if (fl.first > fl.second) return fail(ZR_ERR_INVALID, "bucket range out of range");
+    const zr::GroupInfo& gi = plan->groups[group];
+    if (dst < -1 || dst >= gi.world) return fail(ZR_ERR_INVALID, "dst out of range");
+    if (!valid_dtype(grad_dtype)) return fail(ZR_ERR_INVALID, "unsupported gradient dtype");
+    if (!tiles && !launches) return fail(ZR_ERR_INVALID, "no output pointer");
+    const int64_t tile = reduce_tile(grad_dtype, fused != 0);
+    const std::vector<Seg>* hs = nullptr;
+    const zr_status st = get_host_table(plan, kReduceTable, group, fl.first, fl.second, dst,
+                                        tile, &hs);
+    if (st != ZR_OK) return st;
+    const int64_t nseg = static_cast<int64_t>(hs->size()) - 1;
+    const int64_t total = nseg > 0 ? (*hs)[nseg].tile0 : 0;
+    if (tiles) *tiles = total;
+    if (launches)
+      *launches = nseg > 0 ? launches_for(total, reduce_tile_bytes(tile, gi.world,
+                                                                   dtype_size(grad_dtype),
+                                                                   fused != 0,
+                                                                   with_grad_out != 0))
+                           : 0;
+    return ZR_OK;
+  } catch (...) {
+    return fail(ZR_ERR_OOM, "unexpected host error");
+  }
+}
 
 extern "C" zr_status zr_reduce_scatter_local(const zr_plan* plan, int32_t group,
                                              int64_t bucket, int32_t dst,

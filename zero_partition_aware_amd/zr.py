@@ -94,6 +94,8 @@ _sigs = {
     "zr_plan_grad_start_offset": (c_i32, [c_vp, c_i64, c_i32, _P(c_i64)]),
     "zr_plan_slices": (c_i32, [c_vp, c_i64, _P(_P(zr_slice)), _P(c_i64)]),
     "zr_plan_param_buckets": (c_i32, [c_vp, c_i64, _P(c_i64), _P(c_i64)]),
+    "zr_plan_reduce_launches": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                        c_i32, _P(c_i64), _P(c_i64)]),
     "zr_ipg_accumulate": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
                                   c_i64, c_i64, c_vp]),
     "zr_ipg_accumulate_first": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
@@ -255,6 +257,15 @@ def _dtype_code(t):
     return -1
 
 
+def _dtype_name_code(dt):
+    """ZR_BF16 / ZR_FP32 for "bf16" / "fp32" or the torch dtype."""
+    if dt == "bf16" or (torch is not None and dt is torch.bfloat16):
+        return ZR_BF16
+    if dt == "fp32" or (torch is not None and dt is torch.float32):
+        return ZR_FP32
+    raise ZrError(ZR_ERR_INVALID, f"unsupported gradient dtype {dt!r}")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -370,6 +381,21 @@ def zr_plan_param_buckets(plan, p):
     a, b = c_i64(), c_i64()
     _check(_lib.zr_plan_param_buckets(plan.handle, _i64(p, "p"), ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def zr_plan_reduce_launches(plan, group, bucket_first, bucket_count, dst, grad_dtype,
+                            fused, with_grad_out=False):
+    """(tiles, launches) of a reduce call over buckets [bucket_first,
+    bucket_first + bucket_count) for ``dst``; grad_dtype is "bf16" or
+    "fp32" (or a torch dtype)."""
+    dt = _dtype_name_code(grad_dtype)
+    t, n = c_i64(), c_i64()
+    _check(_lib.zr_plan_reduce_launches(plan.handle, _i32(group, "group"),
+                                        _i64(bucket_first, "bucket_first"),
+                                        _i64(bucket_count, "bucket_count"), _i32(dst, "dst"),
+                                        dt, int(bool(fused)), int(bool(with_grad_out)),
+                                        ctypes.byref(t), ctypes.byref(n)))
+    return t.value, n.value
 
 
 def zr_plan_slices(plan, bucket=-1):
