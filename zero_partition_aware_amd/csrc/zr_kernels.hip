@@ -3,14 +3,16 @@
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
 // LDS staging and no MFMA.  Work is cut into tiles of one "segment" (a merged
 // slice of the plan, a param's piece of an IPG window, a ring chunk): the
-// reduce and Adam kernels take 512 elements per 128-thread workgroup (one
-// 4-element slot per lane), the lighter IPG, copy, ring reduce-scatter and
-// all-gather kernels 1024 (two slots per lane).  By default every workgroup
-// takes exactly one tile, so the hardware dispatcher hands tiles out in
-// address order and the set of DRAM pages being touched at any moment stays
-// compact.  A workgroup finds its tile's segment by a binary search over
-// per-segment tile offsets.  Reduce-kernel tiles start where replica 0's
-// tiles sit on whole 128-byte lines, when the other streams allow it.
+// reduce kernels take 256 elements per one-wave workgroup (512 per two waves
+// for the bf16 fused step), Adam 512 per 128 lanes -- one 4-element slot per
+// lane -- and the lighter IPG, copy, ring reduce-scatter and all-gather
+// kernels 1024 per 128 lanes (two slots per lane).  By default every
+// workgroup takes exactly one tile, so the hardware dispatcher hands tiles
+// out in address order and the set of DRAM pages being touched at any moment
+// stays compact.  A workgroup finds its tile's segment by a binary search
+// over per-segment tile offsets, read through the scalar cache.
+// Reduce-kernel tiles start where replica 0's tiles sit on whole 128-byte
+// lines, when the other streams allow it.
 //
 // Inside a tile each lane owns "slots" of four consecutive elements, and the
 // 64 lanes of a wavefront own 64 consecutive slots, so every load or store
@@ -28,8 +30,9 @@
 //
 // Long selections are cut into several launches of at most ZR_LAUNCH_BYTES
 // of traffic each.  Within one launch the eight XCDs take every eighth tile in
-// dispatch order but run at different speeds (measured: some ~10% slower than
-// others), so in a long launch they drift apart -- by 140k tiles, 290 MB of
+// dispatch order but run at different speeds (measured: the odd XCDs 2-7%
+// slower than the even ones; the reduce kernels weight their shares for it,
+// skew_tile below), so in a long launch they drift apart -- by 140k tiles, 290 MB of
 // every stream, late in a 10 ms launch -- the addresses in flight spread over
 // a widening window, and the launch ends on the slowest XCD.  A kernel
 // boundary brings them back together.  Measured on the fused fp32 8-replica
