@@ -3,7 +3,7 @@ bucket sizes from 1 element to unbounded, align up to 64), random element
 offsets of every stream, bf16 or fp32 replicas; the fused and unfused calls
 on several ranks (and the grid-capped fused call, bit for bit against the
 uncapped one), the per-bucket calls composed, and IPG over a random
-window, each against the oracle (bit-exact; Adam within rel 1e-6 / abs
+window (half as a step's first micro-batch), each against the oracle (bit-exact; Adam within rel 1e-6 / abs
 1e-7; bf16 param = RNE of the GPU's own master)."""
 
 import random
@@ -110,12 +110,22 @@ def _random_case(seed):
         ids = [p for p in range(n) if pg[p] == g]
         pr.shuffle(ids)
         mg = np.zeros(length, np.float32)
-        dmg = to_dev(mg)
+        # half the cases write the window as a step's first micro-batch
+        # (zr_ipg_accumulate_first into NaN, never read): covered elements
+        # must equal the add into zeros, the rest keep their NaN
+        first = pr.random() < 0.5
+        covered = np.zeros(length, bool)
+        for p in ids:
+            lo = max(ref.param_offset[p], base) - base
+            hi = min(ref.param_offset[p] + numels[p], base + length) - base
+            if hi > lo:
+                covered[lo:hi] = True
+        dmg = to_dev(np.where(covered, np.float32(np.nan), mg) if first else mg)
         grads = [_draw(rng, numels[p], bf16) for p in ids]
         if ids:
             ipg_accumulate_oracle(mg, base, ref.param_offset, ids, grads, bf16)
-            zr.zr_ipg_accumulate(plan, ids, [to_dev(x, pr.randint(0, 5)) for x in grads], dmg,
-                                 window_base=base)
+            ipg = zr.zr_ipg_accumulate_first if first else zr.zr_ipg_accumulate
+            ipg(plan, ids, [to_dev(x, pr.randint(0, 5)) for x in grads], dmg, window_base=base)
             assert_bits_equal(host_f32(dmg), mg, f"seed {seed} ipg")
 
 
