@@ -783,6 +783,33 @@ def setup_llama(torch, zr, workloads, ipg=False):
     return step, bytes_per_step, P, cfg, {"fused": bytes_per_step}, "fused", cpu_leg
 
 
+def setup_share(torch, zr, workloads, P):
+    """The fused step on one rank's share of P elements with 8 fp32
+    replicas (one parameter of 8P elements, one bucket), for how the rate
+    depends on the share size: 58 B per partition element."""
+    R = 8
+    plan = zr.zr_plan_buckets([R * P], [0], [(R, 1)], 1 << 62)
+    name = f"share-{P}"
+    reps = [(workloads.device_normal(9_100_000 + r, P, 1e-3, "cuda"), 0) for r in range(R)]
+    master = workloads.device_normal(9_199_000, P, 0.02, "cuda")
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    pbf16 = torch.empty(P, dtype=torch.bfloat16, device="cuda")
+    bytes_per_step = (R * 4 + 26) * P
+
+    def step(i, timer):
+        timer.launch(lambda: zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, master, m, v, pbf16,
+                                                       None, step=i + 1, **HP), "fused")
+
+    step.dispatches = {"fused": reduce_dispatches(zr, plan, 0, 0, "fp32", True)}
+    cfg = {"workload": name, "replicas": R, "partition_elems": P, "grad_dtype": "fp32",
+           "bytes_per_step": bytes_per_step}
+    return step, bytes_per_step, P, cfg, {"fused": bytes_per_step}, "fused", None
+
+
+SHARE_SIZES = {"share-15m": 15_554_976, "share-125m": 125_000_000, "share-500m": 500_000_000,
+               "share-1b": 1_003_782_656}
+
+
 def setup_moe(torch, zr, workloads):
     name = "moe-16l"
     w = workloads.get(name)
@@ -1218,6 +1245,7 @@ def main():
                              "llama3-8b-overlap",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
                              "moe-16l-bucketed-fused", "moe-16l-per-bucket", "moe-16l-per-bucket-graph",
+                             *SHARE_SIZES,
                              "llama3-8b-copy", "gpt2-small-all-ranks",
                              "ring-1gib", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1264,6 +1292,7 @@ def main():
               "llama3-8b-ipg": lambda *a: setup_llama(*a, ipg=True), "moe-16l": setup_moe,
               "moe-16l-bucketed": setup_moe_bucketed,
               "moe-16l-bucketed-fused": lambda *a: setup_moe_bucketed(*a, fused=True),
+              **{k: (lambda P: lambda *a: setup_share(*a, P))(P) for k, P in SHARE_SIZES.items()},
               "llama3-8b-copy": setup_llama_copy,
               "gpt2-small-all-ranks": lambda *a: setup_gpt2(*a, all_ranks=True),
               "moe-16l-per-bucket": lambda *a: setup_moe_bucketed(*a, per_bucket=True),
