@@ -327,7 +327,7 @@ zr_status zr_adam_partition(const zr_adam* h, const float* grad, float* master,
  * covers the last bucket, updated with a zero gradient) are updated.
  * dst >= 0: master, m, v (and param_bf16, grad_out when not null) are that
  * partition's P_g-element buffers.  dst == -1: every rank's step in one
- * launch; the buffers hold all R_g partitions back to back (L_g = R_g*P_g
+ * call; the buffers hold all R_g partitions back to back (L_g = R_g*P_g
  * elements, partition d from element d*P_g), i.e. the group's whole padded
  * flat space.  grad_out receives the reduced gradient.  Each partition's
  * result is the same, bit for bit, as its own call with dst = d. */
@@ -352,9 +352,10 @@ zr_status zr_reduce_scatter_adam_range(const zr_plan* plan, int32_t group,
                                        uint16_t* param_bf16, float* grad_out,
                                        hipStream_t stream);
 
-/* zr_reduce_scatter_adam_capped -- zr_reduce_scatter_adam on a launch of at
- * most max_workgroups workgroups (>= 1; ZR_ERR_INVALID otherwise), each
- * walking the selection's tiles in steps of the grid.  For a reduction that
+/* zr_reduce_scatter_adam_capped -- zr_reduce_scatter_adam on launches of at
+ * most max_workgroups workgroups each (>= 1; ZR_ERR_INVALID otherwise), each
+ * workgroup walking its launch's tiles in steps of the grid (the launches
+ * are the uncapped call's, zr_plan_reduce_launches).  For a reduction that
  * overlaps the backward pass on a second stream ([ZeRO-RS blog] §四: each
  * IPG bucket is reduced as soon as it is full, while backward continues;
  * [Megatron DP] "梯度缓冲区+分桶+overlap"): the cap bounds the workgroup
