@@ -21,6 +21,7 @@ std::map<uintptr_t, size_t>& regions() {
 
 thread_local zr_emu_dim zr_emu_block, zr_emu_thread, zr_emu_grid;
 long long zr_emu_launches = 0;
+unsigned zr_emu_lds_max = 0;
 
 // Launches per kernel instantiation, named by the sanitizer runtime's
 // symbolizer from the kernel's address (this build always runs under it).
@@ -87,7 +88,9 @@ hipError_t hipGetDevice(int* d) {
 }
 hipError_t hipSetDevice(int) { return hipSuccess; }
 hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t attr, int) {
-  *v = attr == hipDeviceAttributeMultiprocessorCount ? 256 : 0;
+  *v = attr == hipDeviceAttributeMultiprocessorCount          ? 256
+       : attr == hipDeviceAttributeMaxSharedMemoryPerMultiprocessor ? 160 * 1024
+                                                                    : 0;
   return hipSuccess;
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }

@@ -77,6 +77,7 @@ inline void zr_emu_nt_store(T v, T* p) {
 // counted per kernel instantiation (zr_emu_count names the kernel from its
 // address) for the coverage report.
 extern long long zr_emu_launches;
+extern unsigned zr_emu_lds_max;  // most dynamic LDS a launch reserved since reset
 void zr_emu_count(void* kernel);
 template <auto K, typename Args>
 inline void zr_emu_launch(unsigned grid, unsigned block, const Args& args) {
@@ -91,5 +92,6 @@ inline void zr_emu_launch(unsigned grid, unsigned block, const Args& args) {
   }
   ++zr_emu_launches;
 }
-#define ZR_KERNEL_LAUNCH(grid, block, stream, args, ...) \
-  zr_emu_launch<&__VA_ARGS__>((grid), (block), (args))
+#define ZR_KERNEL_LAUNCH_LDS(grid, block, lds, stream, args, ...) \
+  (zr_emu_lds_max = zr_emu_lds_max > unsigned(lds) ? zr_emu_lds_max : unsigned(lds), \
+   zr_emu_launch<&__VA_ARGS__>((grid), (block), (args)))

@@ -32,6 +32,7 @@
 void zr_emu_register(const void* p, size_t bytes);
 void zr_emu_unregister(const void* p);
 extern long long zr_emu_launches;
+extern unsigned zr_emu_lds_max;
 std::map<std::string, long long>& zr_emu_coverage();
 
 namespace {
@@ -269,9 +270,11 @@ void reduce_case(Rng& r, int seed) {
       po.push_back(b->f());
     }
     const zr_dtype dt = bf16 ? ZR_BF16 : ZR_FP32;
+    zr_emu_lds_max = 0;
     st = mode == 2 ? zr_reduce_scatter_local_range(pl.h, g, first, last - first, dst, zreps.data(), dt, po.data(), nullptr)
                    : zr_reduce_scatter_local(pl.h, g, mode == 0 ? -1 : first, dst, zreps.data(), dt, po.data(), nullptr);
     CHECK(st == ZR_OK, "seed %d: reduce failed: %s", seed, zr_last_error());
+    CHECK(zr_emu_lds_max == 0, "seed %d: reduce-scatter reserved LDS", seed);
     for (int d = 0; d < nd; ++d) {
       for (int64_t j = 0; j < span; ++j) {
         const uint32_t got = f_bits(outs[d]->f()[j]);
@@ -303,6 +306,7 @@ void reduce_case(Rng& r, int seed) {
     const zr_dtype dt = bf16 ? ZR_BF16 : ZR_FP32;
     uint16_t* pbp = with_pb ? pb.h() : nullptr;
     float* gop = with_go ? go.f() : nullptr;
+    zr_emu_lds_max = 0;
     if (mode == 2)
       st = zr_reduce_scatter_adam_range(pl.h, g, first, last - first, dst, zreps.data(), dt, &h,
                                         th.f(), m.f(), v.f(), pbp, gop, nullptr);
@@ -334,6 +338,16 @@ void reduce_case(Rng& r, int seed) {
       return;
     }
     CHECK(st == ZR_OK, "seed %d: fused failed: %s", seed, zr_last_error());
+    // Uncapped fused calls over 4 or more replicas (the threshold this build
+    // sets) reserve 2L / (2k + 1) bytes of LDS per workgroup, L = 160 KiB,
+    // k = 8 for fp32 and 6 for bf16 replicas; no other launch reserves any.
+    bool launched = false;
+    for (int d = 0; d < nd && !launched; ++d)
+      for (int64_t j = 0; j < span && !launched; ++j) launched = written[d][j] != 0;
+    const unsigned want_lds = launched && cap <= 0 && gi.R >= 4
+        ? unsigned(2 * 160 * 1024 / (2 * (bf16 ? 6 : 8) + 1)) : 0u;
+    CHECK(zr_emu_lds_max == want_lds, "seed %d: LDS reserved %u, want %u", seed, zr_emu_lds_max,
+          want_lds);
     const AdamK k = adam_k(h);
     for (int d = 0; d < nd; ++d)
       for (int64_t j = 0; j < span; ++j) {

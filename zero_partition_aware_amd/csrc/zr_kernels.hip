@@ -107,13 +107,35 @@ namespace {
 #ifndef ZR_NT_STORES
 #define ZR_NT_STORES 1
 #endif
-// Launch of kernel __VA_ARGS__ over `grid` workgroups of `block` lanes on
-// `stream` with the argument block `args` (a CPU build of this file for
-// bounds checking substitutes its own).
-#ifndef ZR_KERNEL_LAUNCH
-#define ZR_KERNEL_LAUNCH(grid, block, stream, args, ...) \
-  __VA_ARGS__<<<(grid), (block), 0, (stream)>>>(args)
+// Workgroups per CU that an uncapped fused launch over 8 or more replicas
+// may hold at once (0 = as many as fit).  The launch reserves LDS it does not
+// use so that no more fit (reduce_lds_bytes below).  A/B-measured, launches
+// interleaved in one process: fp32 (one-wave workgroups) on the 8-replica
+// 1.0e9-element share 6.36 TB/s at 8 against 6.21 with no cap and 5.73 at 6;
+// bf16 (two-wave workgroups) on the 8-replica 15.5M-element share 6.16 at 6
+// against 6.07 with no cap, 6.11 at 8 and 6.06 at 5.  Every other reduce
+// launch lost from any cap: the bf16 reduce-scatter (one-wave) 6.13 with
+// none against 4.64 at 10, the 2-replica fp32 fused MoE expert share 6.02
+// against 5.91 at 13.
+#ifndef ZR_FUSED_WGS_PER_CU_F32
+#define ZR_FUSED_WGS_PER_CU_F32 8
 #endif
+#ifndef ZR_FUSED_WGS_PER_CU_BF16
+#define ZR_FUSED_WGS_PER_CU_BF16 6
+#endif
+#ifndef ZR_FUSED_CAP_MIN_WORLD
+#define ZR_FUSED_CAP_MIN_WORLD 8
+#endif
+// Launch of kernel __VA_ARGS__ over `grid` workgroups of `block` lanes on
+// `stream` with the argument block `args`, reserving `lds` bytes of dynamic
+// LDS per workgroup (a CPU build of this file for bounds checking
+// substitutes its own).
+#ifndef ZR_KERNEL_LAUNCH_LDS
+#define ZR_KERNEL_LAUNCH_LDS(grid, block, lds, stream, args, ...) \
+  __VA_ARGS__<<<(grid), (block), (lds), (stream)>>>(args)
+#endif
+#define ZR_KERNEL_LAUNCH(grid, block, stream, args, ...) \
+  ZR_KERNEL_LAUNCH_LDS(grid, block, 0, stream, args, __VA_ARGS__)
 constexpr int kThreads = ZR_THREADS;
 constexpr int VE = 4;  // elements per lane slot
 // Cache-line size the reduce kernels align replica tiles to, and the largest
@@ -1280,6 +1302,30 @@ zr_status device_info(int* dev, int* cus) {
   return ZR_OK;
 }
 
+std::atomic<int> g_lds_per_cu[64];  // per device, 0 until first queried
+
+// Dynamic LDS a reduce launch reserves per workgroup: 0, or for an uncapped
+// fused launch over ZR_FUSED_CAP_MIN_WORLD or more replicas enough that at
+// most k = ZR_FUSED_WGS_PER_CU_* workgroups fit in a CU's LDS L.  The value
+// 2L / (2k + 1) sits mid-way in the range (L / (k + 1), L / k] that admits
+// exactly k, so rounding to the allocation granularity cannot tip it.
+zr_status reduce_lds_bytes(int dev, bool fused, bool bf16, int world, bool capped,
+                           unsigned* lds) {
+  *lds = 0;
+  const int k = bf16 ? ZR_FUSED_WGS_PER_CU_BF16 : ZR_FUSED_WGS_PER_CU_F32;
+  if (!fused || capped || k <= 0 || world < ZR_FUSED_CAP_MIN_WORLD) return ZR_OK;
+  int n = g_lds_per_cu[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    const hipError_t e =
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return fail(ZR_ERR_HIP, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e));
+    n = n > 0 ? n : -1;
+    g_lds_per_cu[dev].store(n, std::memory_order_relaxed);
+  }
+  if (n > 0) *lds = static_cast<unsigned>(2 * static_cast<int64_t>(n) / (2 * k + 1));
+  return ZR_OK;
+}
+
 // One workgroup per tile (ZR_GRID_PER_CU == 0), else a capped grid-stride
 // grid.  Kernels loop over tiles either way, so any grid size is correct.
 unsigned grid_for(int64_t tiles, int cus) {
@@ -1435,14 +1481,16 @@ zr_status adam_consts(const zr_adam* h, AdamConsts* k) {
 
 template <typename InT, bool kFused>
 zr_status launch_reduce_t(const RedArgs& a, int R, bool div, bool dword, unsigned grid,
-                          hipStream_t st) {
-#define ZR_LAUNCH(RR, DD)                                                           \
-  do {                                                                              \
-    constexpr int kTH = red_threads<InT, kFused>();                                 \
-    if (dword)                                                                      \
-      ZR_KERNEL_LAUNCH(grid, kTH, st, a, reduce_kernel<InT, RR, DD, kFused, true>); \
-    else                                                                            \
-      ZR_KERNEL_LAUNCH(grid, kTH, st, a, reduce_kernel<InT, RR, DD, kFused, false>);\
+                          unsigned lds, hipStream_t st) {
+#define ZR_LAUNCH(RR, DD)                                                          \
+  do {                                                                             \
+    constexpr int kTH = red_threads<InT, kFused>();                                \
+    if (dword)                                                                     \
+      ZR_KERNEL_LAUNCH_LDS(grid, kTH, lds, st, a,                                  \
+                           reduce_kernel<InT, RR, DD, kFused, true>);              \
+    else                                                                           \
+      ZR_KERNEL_LAUNCH_LDS(grid, kTH, lds, st, a,                                  \
+                           reduce_kernel<InT, RR, DD, kFused, false>);             \
   } while (0)
   if (div) {
     switch (R) {
@@ -1645,6 +1693,9 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     st = get_dev_table(plan, kReduceTable, group, first, last, dst, tile, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
+  unsigned lds = 0;
+  st = reduce_lds_bytes(device, fused, dt == ZR_BF16, gi.world, max_wgs > 0, &lds);
+  if (st != ZR_OK) return st;
   for (int64_t i = 0; i < nl; ++i) {
     a.tile_base = launch_first(total, nl, i);
     a.tile_end = launch_first(total, nl, i + 1);
@@ -1660,11 +1711,11 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
         : a.skew ? static_cast<unsigned>(skew_grid(n))
                  : grid_for(n, cus);
     if (dt == ZR_BF16)
-      st = fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, dword, grid, stream)
-                 : launch_reduce_t<uint16_t, false>(a, gi.world, div, dword, grid, stream);
+      st = fused ? launch_reduce_t<uint16_t, true>(a, gi.world, div, dword, grid, lds, stream)
+                 : launch_reduce_t<uint16_t, false>(a, gi.world, div, dword, grid, lds, stream);
     else
-      st = fused ? launch_reduce_t<float, true>(a, gi.world, div, dword, grid, stream)
-                 : launch_reduce_t<float, false>(a, gi.world, div, dword, grid, stream);
+      st = fused ? launch_reduce_t<float, true>(a, gi.world, div, dword, grid, lds, stream)
+                 : launch_reduce_t<float, false>(a, gi.world, div, dword, grid, lds, stream);
     if (st != ZR_OK) return st;
   }
   return ZR_OK;
