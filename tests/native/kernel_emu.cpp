@@ -49,6 +49,27 @@ int g_failures = 0;
     }                                                                  \
   } while (0)
 
+// Workgroups per CU an uncapped reduce launch is held to (0 = no cap), as
+// the library states it: fp32 fused 8, bf16 fused 6, bf16 reduce-scatter 20,
+// fp32 reduce-scatter 12 at 8 replicas; fp32 fused 18 and fp32
+// reduce-scatter 28 at 2 replicas; no other shape.
+int want_wgs_per_cu(bool bf16, bool fused, int R) {
+  if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
+  if (R == 2 && !bf16) return fused ? 18 : 28;
+  return 0;
+}
+
+// A call that launched the reduce kernel reserved 2L / (2k + 1) bytes of LDS
+// per workgroup for L = 160 KiB (the emulated device's LDS per CU) when k > 0,
+// and nothing otherwise; no launch of the call reserved more.
+void check_lds(int seed, int nd, int64_t span, const std::vector<std::vector<char>>& written, int k) {
+  bool launched = false;
+  for (int d = 0; d < nd && !launched; ++d)
+    for (int64_t j = 0; j < span && !launched; ++j) launched = written[d][j] != 0;
+  const unsigned want = launched && k > 0 ? unsigned(2 * 160 * 1024 / (2 * k + 1)) : 0u;
+  CHECK(zr_emu_lds_max == want, "seed %d: LDS reserved %u, want %u", seed, zr_emu_lds_max, want);
+}
+
 struct Rng {
   uint64_t s;
   explicit Rng(uint64_t seed) : s(seed * 0x9E3779B97F4A7C15ull + 1) {}
@@ -274,7 +295,7 @@ void reduce_case(Rng& r, int seed) {
     st = mode == 2 ? zr_reduce_scatter_local_range(pl.h, g, first, last - first, dst, zreps.data(), dt, po.data(), nullptr)
                    : zr_reduce_scatter_local(pl.h, g, mode == 0 ? -1 : first, dst, zreps.data(), dt, po.data(), nullptr);
     CHECK(st == ZR_OK, "seed %d: reduce failed: %s", seed, zr_last_error());
-    CHECK(zr_emu_lds_max == 0, "seed %d: reduce-scatter reserved LDS", seed);
+    check_lds(seed, nd, span, written, want_wgs_per_cu(bf16, false, gi.R));
     for (int d = 0; d < nd; ++d) {
       for (int64_t j = 0; j < span; ++j) {
         const uint32_t got = f_bits(outs[d]->f()[j]);
@@ -338,16 +359,7 @@ void reduce_case(Rng& r, int seed) {
       return;
     }
     CHECK(st == ZR_OK, "seed %d: fused failed: %s", seed, zr_last_error());
-    // Uncapped fused calls over 4 or more replicas (the threshold this build
-    // sets) reserve 2L / (2k + 1) bytes of LDS per workgroup, L = 160 KiB,
-    // k = 8 for fp32 and 6 for bf16 replicas; no other launch reserves any.
-    bool launched = false;
-    for (int d = 0; d < nd && !launched; ++d)
-      for (int64_t j = 0; j < span && !launched; ++j) launched = written[d][j] != 0;
-    const unsigned want_lds = launched && cap <= 0 && gi.R >= 4
-        ? unsigned(2 * 160 * 1024 / (2 * (bf16 ? 6 : 8) + 1)) : 0u;
-    CHECK(zr_emu_lds_max == want_lds, "seed %d: LDS reserved %u, want %u", seed, zr_emu_lds_max,
-          want_lds);
+    check_lds(seed, nd, span, written, cap <= 0 ? want_wgs_per_cu(bf16, true, gi.R) : 0);
     const AdamK k = adam_k(h);
     for (int d = 0; d < nd; ++d)
       for (int64_t j = 0; j < span; ++j) {

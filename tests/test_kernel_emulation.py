@@ -36,8 +36,6 @@ def _build(tmp_path, kernels_src, name):
            # an XCD-weighted order of 2-round cycles from 4 replicas up, so
            # that short launches hold whole cycles and both orders run
            "-DZR_XCD_SKEW=2", "-DZR_XCD_SKEW_MIN_WORLD=4",
-           # the occupancy cap's LDS reservation from 4 replicas up too
-           "-DZR_FUSED_CAP_MIN_WORLD=4",
            "-I", os.path.join(NATIVE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-I", "/opt/rocm/include",
            "-x", "c++", kernels_src, "-x", "none", os.path.join(CSRC, "zr_plan.cpp"),

@@ -107,24 +107,13 @@ namespace {
 #ifndef ZR_NT_STORES
 #define ZR_NT_STORES 1
 #endif
-// Workgroups per CU that an uncapped fused launch over 8 or more replicas
-// may hold at once (0 = as many as fit).  The launch reserves LDS it does not
-// use so that no more fit (reduce_lds_bytes below).  A/B-measured, launches
-// interleaved in one process: fp32 (one-wave workgroups) on the 8-replica
-// 1.0e9-element share 6.36 TB/s at 8 against 6.21 with no cap and 5.73 at 6;
-// bf16 (two-wave workgroups) on the 8-replica 15.5M-element share 6.16 at 6
-// against 6.07 with no cap, 6.11 at 8 and 6.06 at 5.  Every other reduce
-// launch lost from any cap: the bf16 reduce-scatter (one-wave) 6.13 with
-// none against 4.64 at 10, the 2-replica fp32 fused MoE expert share 6.02
-// against 5.91 at 13.
-#ifndef ZR_FUSED_WGS_PER_CU_F32
-#define ZR_FUSED_WGS_PER_CU_F32 8
-#endif
-#ifndef ZR_FUSED_WGS_PER_CU_BF16
-#define ZR_FUSED_WGS_PER_CU_BF16 6
-#endif
-#ifndef ZR_FUSED_CAP_MIN_WORLD
-#define ZR_FUSED_CAP_MIN_WORLD 8
+// Workgroups per CU that an uncapped reduce launch may hold at once (the
+// launch reserves LDS it does not use so that no more fit: reduce_lds_bytes
+// below).  Fewer streams in flight than the register limit allows measured
+// faster for the shapes the table lists; every other shape, and grid-capped
+// calls, keep the register-limited occupancy.  0 turns the table off.
+#ifndef ZR_RED_WGS_CAP
+#define ZR_RED_WGS_CAP 1
 #endif
 // Launch of kernel __VA_ARGS__ over `grid` workgroups of `block` lanes on
 // `stream` with the argument block `args`, reserving `lds` bytes of dynamic
@@ -1304,16 +1293,42 @@ zr_status device_info(int* dev, int* cus) {
 
 std::atomic<int> g_lds_per_cu[64];  // per device, 0 until first queried
 
+// Workgroups per CU for an uncapped reduce launch of R replicas (0 = as many
+// as the registers allow), by replica type and kernel.  Each value is the
+// best of an interleaved in-process sweep of the cap (launches alternating,
+// 12 rounds, one session per line), listed with what no cap gives and with
+// its neighbours, in TB/s:
+//   fp32 fused, R = 8 (Llama-3-8B share): 8 -> 6.45; none 6.22, 10 6.42,
+//     9 6.42, 7 6.29
+//   bf16 fused, R = 8 (GPT-2 share, two-wave workgroups): 6 -> 6.11; none
+//     6.07, 8 6.08, 7 6.10, 5 6.05
+//   bf16 reduce-scatter, R = 8 (GPT-2, every partition): 20 -> 6.54; none
+//     6.31, 24 6.39, 22 6.43, 18 6.55
+//   fp32 reduce-scatter, R = 8 (MoE dense share): 12 -> 6.40; none 6.20,
+//     14 6.27, 13 6.32, 11 6.14
+//   fp32 fused, R = 2 (MoE expert share): 18 -> 6.24; none 6.11, 20 6.23,
+//     17 6.25, 16 6.25
+//   fp32 reduce-scatter, R = 2 (MoE expert share): 28 -> 6.67; none 6.22,
+//     32 6.23, 30 6.68, 26 6.70 (another session: none 6.21, 24 6.20,
+//     20 5.65)
+// Other replica counts and types were not measured and take no cap.
+int reduce_wgs_per_cu(bool bf16, bool fused, int R) {
+  if (!ZR_RED_WGS_CAP) return 0;
+  if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
+  if (R == 2 && !bf16) return fused ? 18 : 28;
+  return 0;
+}
+
 // Dynamic LDS a reduce launch reserves per workgroup: 0, or for an uncapped
-// fused launch over ZR_FUSED_CAP_MIN_WORLD or more replicas enough that at
-// most k = ZR_FUSED_WGS_PER_CU_* workgroups fit in a CU's LDS L.  The value
-// 2L / (2k + 1) sits mid-way in the range (L / (k + 1), L / k] that admits
-// exactly k, so rounding to the allocation granularity cannot tip it.
+// launch with a table entry k enough that at most k workgroups fit in a CU's
+// LDS L.  The value 2L / (2k + 1) sits mid-way in the range
+// (L / (k + 1), L / k] that admits exactly k, so rounding to the allocation
+// granularity cannot tip it.
 zr_status reduce_lds_bytes(int dev, bool fused, bool bf16, int world, bool capped,
                            unsigned* lds) {
   *lds = 0;
-  const int k = bf16 ? ZR_FUSED_WGS_PER_CU_BF16 : ZR_FUSED_WGS_PER_CU_F32;
-  if (!fused || capped || k <= 0 || world < ZR_FUSED_CAP_MIN_WORLD) return ZR_OK;
+  const int k = reduce_wgs_per_cu(bf16, fused, world);
+  if (capped || k <= 0) return ZR_OK;
   int n = g_lds_per_cu[dev].load(std::memory_order_relaxed);
   if (n == 0) {
     const hipError_t e =
