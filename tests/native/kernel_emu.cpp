@@ -51,11 +51,11 @@ int g_failures = 0;
 
 // Workgroups per CU an uncapped reduce launch is held to (0 = no cap), as
 // the library states it: fp32 fused 8, bf16 fused 6, bf16 reduce-scatter 20,
-// fp32 reduce-scatter 12 at 8 replicas; fp32 fused 18 and fp32
-// reduce-scatter 28 at 2 replicas; no other shape.
+// fp32 reduce-scatter 12 at 8 replicas; fp32 fused 18 at 2 replicas; no
+// other shape.
 int want_wgs_per_cu(bool bf16, bool fused, int R) {
   if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
-  if (R == 2 && !bf16) return fused ? 18 : 28;
+  if (R == 2 && !bf16 && fused) return 18;
   return 0;
 }
 

@@ -1307,15 +1307,16 @@ std::atomic<int> g_lds_per_cu[64];  // per device, 0 until first queried
 //   fp32 reduce-scatter, R = 8 (MoE dense share): 12 -> 6.40; none 6.20,
 //     14 6.27, 13 6.32, 11 6.14
 //   fp32 fused, R = 2 (MoE expert share): 18 -> 6.24; none 6.11, 20 6.23,
-//     17 6.25, 16 6.25
-//   fp32 reduce-scatter, R = 2 (MoE expert share): 28 -> 6.67; none 6.22,
-//     32 6.23, 30 6.68, 26 6.70 (another session: none 6.21, 24 6.20,
-//     20 5.65)
-// Other replica counts and types were not measured and take no cap.
+//     17 6.25, 16 6.25; its range calls as buckets complete 18 -> 6.15
+//     against 6.05
+// The fp32 reduce-scatter at R = 2 takes none: 28 per CU gave +7% on the
+// whole MoE expert share (6.67 against 6.22) but -4.5% on the same share's
+// range calls as buckets complete (5.88 against 6.15).  Other replica counts
+// and types were not measured and take no cap.
 int reduce_wgs_per_cu(bool bf16, bool fused, int R) {
   if (!ZR_RED_WGS_CAP) return 0;
   if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
-  if (R == 2 && !bf16) return fused ? 18 : 28;
+  if (R == 2 && !bf16 && fused) return 18;
   return 0;
 }
 
