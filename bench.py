@@ -27,6 +27,7 @@ import argparse
 import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -461,6 +462,66 @@ def setup_ring_allreduce(torch, zr, workloads):
     cfg = {"workload": "ring-1gib-allreduce", "ranks": N, "chunk_elems": C,
            "bytes_per_step": b}
     return step, b, M * N, cfg, {"ring_rs": rs, "ring_ag": ag}, "ring_rs", None
+
+
+def run_placement(torch, zr, workloads, args):
+    """The headline call on freshly allocated buffers, ``--sets`` times in
+    one process: each set allocates rank 0's 8 fp32 replica windows and its
+    state as the headline does, times ``--calls`` calls (each between its own
+    pair of events, after two untimed ones), then frees everything and
+    returns the memory to the driver before the next set.  The virtual
+    addresses usually repeat; the physical pages behind them need not, so the
+    spread over the sets is the part of the headline's run-to-run spread that
+    follows the allocation."""
+    name = "llama3-8b"
+    w = workloads.get(name)
+    plan = zr.zr_plan_buckets(w.numels, w.param_groups, w.groups, w.reduce_bucket_size)
+    T, L, P, D = zr.zr_plan_group_info(plan, 0)
+    R = w.groups[0][0]
+    byts = (R * 4 + 26) * P
+    sets = []
+    for s_ in range(args.sets):
+        mgs = [workloads.device_normal(workloads.seed_for(name, r, 9), P, 2 * w.grad_sigma, "cuda")
+               for r in range(R)]
+        master = workloads.device_normal(workloads.seed_for(name, 0, master=True), P,
+                                          w.master_sigma, "cuda")
+        m, v = torch.zeros_like(master), torch.zeros_like(master)
+        pbf16 = torch.empty(P, dtype=torch.bfloat16, device="cuda")
+        reps = [(x, 0) for x in mgs]
+        t = 0
+        for _ in range(2):
+            t += 1
+            zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, master, m, v, pbf16, None,
+                                      step=t, **HP)
+        torch.cuda.synchronize()
+        rates = []
+        for _ in range(args.calls):
+            t += 1
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            zr.zr_reduce_scatter_adam(plan, 0, -1, 0, reps, master, m, v, pbf16, None,
+                                      step=t, **HP)
+            b_.record()
+            torch.cuda.synchronize()
+            rates.append(byts / (a_.elapsed_time(b_) * 1e-3) / 1e9)
+        ptrs = [x.data_ptr() for x in mgs] + [master.data_ptr(), m.data_ptr(), v.data_ptr()]
+        sets.append({"median_GBps": round(statistics.median(rates), 1),
+                     "min_GBps": round(min(rates), 1), "max_GBps": round(max(rates), 1),
+                     "lowest_address": hex(min(ptrs))})
+        print(f"placement set {s_}: median {sets[-1]['median_GBps']} GB/s "
+              f"(min {sets[-1]['min_GBps']}, max {sets[-1]['max_GBps']}), lowest address "
+              f"{sets[-1]['lowest_address']}", file=sys.stderr, flush=True)
+        del mgs, master, m, v, pbf16, reps
+        torch.cuda.empty_cache()
+    med = [x["median_GBps"] for x in sets]
+    print(json.dumps({"metric": "achieved HBM GB/s of the headline call per fresh allocation",
+                      "value": None, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                      "data": "synthetic",
+                      "config": {"workload": "llama3-8b-placement", "partition_elems": P,
+                                 "replicas": R, "bytes_per_call": byts, "sets": args.sets,
+                                 "calls_per_set": args.calls},
+                      "sets": sets, "min_of_medians": min(med), "max_of_medians": max(med),
+                      "spread": round(max(med) / min(med) - 1, 4)}), flush=True)
 
 
 def run_overlap(torch, zr, workloads, args):
@@ -1242,7 +1303,7 @@ def main():
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "gpt2-small", "gpt2-small-unfused", "gpt2-small-copy",
                              "gpt2-small-allgather", "gpt2-small-dp", "ring-1gib-allreduce",
-                             "llama3-8b-overlap",
+                             "llama3-8b-overlap", "llama3-8b-placement",
                              "llama3-8b", "llama3-8b-ipg", "moe-16l", "moe-16l-bucketed",
                              "moe-16l-bucketed-fused", "moe-16l-per-bucket", "moe-16l-per-bucket-graph",
                              *SHARE_SIZES,
@@ -1268,6 +1329,10 @@ def main():
                     default=[0],
                     help="compute units given to the reduction stream, the rest to the "
                          "backward stream (llama3-8b-overlap; 0 = no partition)")
+    ap.add_argument("--sets", type=int, default=10,
+                    help="fresh buffer allocations (llama3-8b-placement)")
+    ap.add_argument("--calls", type=int, default=8,
+                    help="timed calls per allocation (llama3-8b-placement)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1282,6 +1347,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "llama3-8b-overlap":
         run_overlap(torch, zr, workloads, args)
+        return
+    if args.workload == "llama3-8b-placement":
+        run_placement(torch, zr, workloads, args)
         return
     setups = {"gpt2-small": setup_gpt2, "llama3-8b": setup_llama,
               "gpt2-small-unfused": setup_gpt2_unfused,
