@@ -1,7 +1,9 @@
 // HIP kernels and their C-ABI entry points for CDNA4 (gfx950).
 //
 // Every kernel here is an HBM-bound stream: no data is reused, so there is no
-// LDS staging and no MFMA.  Work is cut into tiles of one "segment" (a merged
+// LDS staging and no MFMA (the reduce launches only reserve LDS, to hold a CU
+// to a measured number of their workgroups: reduce_wgs_per_cu).  Work is cut
+// into tiles of one "segment" (a merged
 // slice of the plan, a param's piece of an IPG window, a ring chunk): the
 // reduce kernels take 256 elements per one-wave workgroup (512 per two waves
 // for the bf16 fused step), Adam 512 per 128 lanes -- one 4-element slot per
