@@ -1340,6 +1340,8 @@ def main():
               "GPU's HBM and the reduction is a local kernel, so there is no multi-GPU "
               "run of this benchmark.", file=sys.stderr)
         sys.exit(2)
+    if args.sets < 1 or args.calls < 1:
+        ap.error("--sets and --calls must be at least 1")
 
     import torch
     from zero_partition_aware_amd import workloads, zr

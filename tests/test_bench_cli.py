@@ -29,5 +29,13 @@ def test_help_lists_the_workloads():
     out = _run(["--help"])
     assert out.returncode == 0
     for w in ("headline", "llama3-8b", "gpt2-small", "moe-16l", "ring-1gib",
-              "llama3-8b-ipg", "share-1b"):
+              "llama3-8b-ipg", "share-1b", "llama3-8b-placement"):
         assert w in out.stdout
+
+
+def test_placement_needs_a_set_and_a_call():
+    for args in (["--sets", "0"], ["--calls", "0"]):
+        out = _run(["--workload", "llama3-8b-placement", *args])
+        assert out.returncode == 2, (args, out.stdout, out.stderr)
+        assert "at least 1" in out.stderr
+        assert out.stdout == ""
