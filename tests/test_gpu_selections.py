@@ -1,7 +1,7 @@
 """Large rank selections of one to three segments -- one slice, a slice plus
 the last partition's padding, a share cut by a bucket border -- checked on
 every element against the oracle, fused and unfused, bf16 and fp32, with 4
-replicas (equal XCD shares) and 8 (the XCD-weighted order), including
+and 8 replicas (both in the XCD-weighted order), including
 selections cut into several launches (a launch carries at most ~2 GiB of
 traffic).  Reduced gradients bit-exact; Adam within rel 1e-6 / abs 1e-7 (v
 relative only); bf16 param = RNE of the kernel's own master.
@@ -128,7 +128,7 @@ def test_two_segments_cut_by_a_bucket_border(fused, is_bf16):
 
 @pytest.mark.parametrize("is_bf16", [False, True])
 def test_eight_replicas_weighted_order(is_bf16):
-    # 8 replicas of 8,389,000 elements: the XCD-weighted order, fused and not
+    # 8 replicas of 8,389,000 elements, fused and not
     _run([8 * 8_389_000], 8, 1 << 40, 5, is_bf16, True, 4, 1, 1)
     _run([8 * 8_389_000], 8, 1 << 40, 6, is_bf16, False, 5, 1, 1)
     _free()

@@ -1,4 +1,4 @@
-"""The XCD-weighted tile order of the reduce kernels.  Selections of 8 or more
+"""The XCD-weighted tile order of the reduce kernels.  Selections of 2 or more
 replicas hand their tiles out in cycles of 256 workgroups of which the 4
 odd-slot ones of the last 8 take no tile; a launch ends after the workgroup
 that holds its last tile.  Launches whose tile counts end at every kind of
@@ -6,8 +6,8 @@ place in a cycle (first workgroup, mid-cycle, the last 8 with and without
 their idle slots) must give, element by element, what the grid-capped call
 (equal shares, a grid-stride walk) gives and the oracle: reduced gradient
 bit-exact, Adam within rel 1e-6 / abs 1e-7 (v relative only), bf16 param =
-RNE of the kernel's own master.  Fused bf16 and fp32, and the bf16
-reduce-scatter."""
+RNE of the kernel's own master.  Fused bf16 and fp32 and the bf16
+reduce-scatter at 8 replicas; fused fp32 and the fp32 reduce-scatter at 2."""
 
 import numpy as np
 import pytest
@@ -27,7 +27,6 @@ from tests._gpu import assert_bits_equal, assert_within, host_f32, host_u16  # n
 
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
 DEV = "cuda"
-R = 8
 CYCLE = 252            # tiles per cycle of 256 workgroups
 
 
@@ -37,9 +36,10 @@ def _partition_for_tiles(tiles, tile):
     return tiles * tile - 63
 
 
-@pytest.mark.parametrize("is_bf16,fused", [(False, True), (True, True), (True, False)])
+@pytest.mark.parametrize("R,is_bf16,fused", [(8, False, True), (8, True, True), (8, True, False),
+                                            (2, False, True), (2, False, False)])
 @pytest.mark.parametrize("rem", [1, 100, 247, 248, 249, 251, 252])
-def test_every_cycle_tail_matches_equal_shares_and_oracle(is_bf16, fused, rem):
+def test_every_cycle_tail_matches_equal_shares_and_oracle(R, is_bf16, fused, rem):
     tile = 512 if is_bf16 and fused else 256
     tiles = 2 * CYCLE + rem
     P = _partition_for_tiles(tiles, tile)
@@ -48,10 +48,10 @@ def test_every_cycle_tail_matches_equal_shares_and_oracle(is_bf16, fused, rem):
     ref = plan_oracle(numels, [0], [(R, 1)], 1 << 40)
     plan = zr.zr_plan_buckets(numels, [0], [(R, 1)], 1 << 40)
     assert ref.groups[0].part_numel == P
-    dst = 3
+    dst = min(3, R - 1)
     lo = dst * P
     dt = "bf16" if is_bf16 else "fp32"
-    seed = 700 + rem + (10 if is_bf16 else 0) + (20 if fused else 0)
+    seed = 700 + rem + (10 if is_bf16 else 0) + (20 if fused else 0) + (1000 if R == 2 else 0)
     wins = [workloads.device_normal(seed * 100 + r, P, 1e-3, DEV, dt) for r in range(R)]
     reps = [(w, lo) for w in wins]
     xs = [host_u16(w) if is_bf16 else host_f32(w) for w in wins]

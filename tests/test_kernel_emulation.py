@@ -33,9 +33,10 @@ def _build(tmp_path, kernels_src, name):
     cmd = [CLANG, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-ffp-contract=off",
            "-Wno-align-mismatch", "-D__HIP_PLATFORM_AMD__", "-DZR_LAUNCH_BYTES=65536",
-           # an XCD-weighted order of 2-round cycles from 4 replicas up, so
-           # that short launches hold whole cycles and both orders run
-           "-DZR_XCD_SKEW=2", "-DZR_XCD_SKEW_MIN_WORLD=4",
+           # an XCD-weighted order of 2-round cycles (from 2 replicas up, as
+           # in the library), so that short launches hold whole cycles; one
+           # replica and capped calls keep equal shares
+           "-DZR_XCD_SKEW=2",
            "-I", os.path.join(NATIVE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-I", "/opt/rocm/include",
            "-x", "c++", kernels_src, "-x", "none", os.path.join(CSRC, "zr_plan.cpp"),

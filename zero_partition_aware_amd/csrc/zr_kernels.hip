@@ -393,13 +393,18 @@ struct Seg {
 // process on two machines, K = 32 against equal shares: 8 fp32 replicas on
 // the 1.0e9-element share +0.3-0.7%, 8 bf16 replicas fused on the
 // 15.5M-element share +0.75-1.0%, the 8-replica bf16 reduce-scatter
-// +1.9-2.0%, but the 2-replica fp32 MoE expert call -1.3%; so the order is
-// taken by selections of at least ZR_XCD_SKEW_MIN_WORLD replicas.
+// +1.9-2.4%.  With the workgroups-per-CU table in place, 2 replicas gain
+// too (two machines): the fp32 MoE expert share fused +2.7-3.9%, its
+// reduce-scatter +7.1-7.5%, and the same share's range calls as buckets
+// complete +1.9-2.0% (reduce-scatter) and +2.1% (fused).  (Before that
+// table, equal shares had measured 1.3% faster for the fused 2-replica
+// call.)  Selections of at least ZR_XCD_SKEW_MIN_WORLD replicas take the
+// weighted order.
 #ifndef ZR_XCD_SKEW
 #define ZR_XCD_SKEW 32
 #endif
 #ifndef ZR_XCD_SKEW_MIN_WORLD
-#define ZR_XCD_SKEW_MIN_WORLD 8
+#define ZR_XCD_SKEW_MIN_WORLD 2
 #endif
 constexpr int kXcdSkew = ZR_XCD_SKEW;
 // Tile offset (within the launch) of workgroup b, or -1 for no tile.
