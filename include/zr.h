@@ -221,6 +221,23 @@ zr_status zr_plan_reduce_launches(const zr_plan* plan, int32_t group,
                                   int32_t with_grad_out, int64_t* tiles,
                                   int64_t* launches);
 
+/* How an uncapped reduce call shares the chip (host only; no GPU needed),
+ * for `world` replicas of grad_dtype through zr_reduce_scatter_local and its
+ * range form (fused = 0) or zr_reduce_scatter_adam and its range and
+ * no-allocation forms (fused = 1).  *wgs_per_cu: how many of the call's
+ * workgroups one CU may hold at once; 0 = as many as the kernel's registers
+ * allow, otherwise each launch reserves LDS it never touches, so that no
+ * more fit.  *weighted: 1 when each launch gives the odd-numbered XCDs 31/32
+ * of the tiles the even-numbered ones take, 0 for equal shares.  Grid-capped
+ * calls (zr_reduce_scatter_adam_capped) reserve no LDS and take equal shares
+ * whatever this says.  Neither changes any result; both matter to a caller
+ * that runs the reduction beside other work on the GPU, as the method does
+ * when it overlaps the reduction with the backward ([ZeRO-RS blog §四]:
+ * overlap_comm).  Either output pointer may be null, not both.
+ * Errors: ZR_ERR_INVALID for world < 1 or an unsupported dtype. */
+zr_status zr_reduce_launch_occupancy(zr_dtype grad_dtype, int32_t fused, int32_t world,
+                                     int32_t* wgs_per_cu, int32_t* weighted);
+
 /* ------------------------------------------------------------- kernels --- */
 
 /* zr_ipg_accumulate -- add each listed param's gradient into the contiguous

@@ -420,3 +420,26 @@ def test_reduce_launch_shape_follows_the_stated_rules():
         zr.zr_plan_reduce_launches(plan, 0, 0, 1, 99, "fp32", True)
     with pytest.raises(zr.ZrError):
         zr.zr_plan_reduce_launches(plan, 0, 0, 1, 0, "fp16", True)
+
+
+def test_reduce_launch_occupancy_follows_the_stated_table():
+    """zr_reduce_launch_occupancy against the table the library states: at
+    8 replicas fp32 fused 8, bf16 fused 6, bf16 reduce-scatter 20, fp32
+    reduce-scatter 12 workgroups per CU; at 2 replicas fp32 fused 18; every
+    other shape 0 (register-limited); the XCD-weighted order from 2 replicas
+    up."""
+    def rule(bf16, fused, world):
+        if world == 8:
+            return (6 if bf16 else 8) if fused else (20 if bf16 else 12)
+        if world == 2 and not bf16 and fused:
+            return 18
+        return 0
+
+    for world in list(range(1, 18)) + [64]:
+        for bf16 in (False, True):
+            for fused in (False, True):
+                got = zr.zr_reduce_launch_occupancy("bf16" if bf16 else "fp32", fused, world)
+                assert got == (rule(bf16, fused, world), world >= 2), (world, bf16, fused)
+    for bad in ((0, "fp32"), (-3, "bf16"), (8, "fp16")):
+        with pytest.raises(zr.ZrError):
+            zr.zr_reduce_launch_occupancy(bad[1], True, bad[0])

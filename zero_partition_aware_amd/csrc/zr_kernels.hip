@@ -1327,6 +1327,12 @@ int reduce_wgs_per_cu(bool bf16, bool fused, int R) {
   return 0;
 }
 
+// Whether an uncapped reduce launch over `world` replicas hands its tiles out
+// in the XCD-weighted order (skew_tile) rather than in equal shares.
+bool xcd_weighted(int world) {
+  return kXcdSkew > 0 && ZR_GRID_PER_CU == 0 && world >= ZR_XCD_SKEW_MIN_WORLD;
+}
+
 // Dynamic LDS a reduce launch reserves per workgroup: 0, or for an uncapped
 // launch with a table entry k enough that at most k workgroups fit in a CU's
 // LDS L.  The value 2L / (2k + 1) sits mid-way in the range
@@ -1727,8 +1733,7 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     const int64_t n = a.tile_end - a.tile_base;
     // Uncapped launches of one tile per workgroup over enough replicas take
     // the XCD-weighted order.
-    a.skew = kXcdSkew > 0 && max_wgs <= 0 && ZR_GRID_PER_CU == 0 &&
-             gi.world >= ZR_XCD_SKEW_MIN_WORLD;
+    a.skew = max_wgs <= 0 && xcd_weighted(gi.world);
     const unsigned grid = max_wgs > 0
         ? static_cast<unsigned>(std::min<int64_t>(grid_for(n, cus), max_wgs))
         : a.skew ? static_cast<unsigned>(skew_grid(n))
@@ -1800,6 +1805,18 @@ extern "C" zr_status zr_plan_reduce_launches(const zr_plan* plan, int32_t group,
   } catch (...) {
     return fail(ZR_ERR_OOM, "unexpected host error");
   }
+}
+
+extern "C" zr_status zr_reduce_launch_occupancy(zr_dtype grad_dtype, int32_t fused,
+                                                int32_t world, int32_t* wgs_per_cu,
+                                                int32_t* weighted) {
+  zr::clear_error();
+  if (!valid_dtype(grad_dtype)) return fail(ZR_ERR_INVALID, "unsupported gradient dtype");
+  if (world < 1) return fail(ZR_ERR_INVALID, "world must be at least 1");
+  if (!wgs_per_cu && !weighted) return fail(ZR_ERR_INVALID, "no output pointer");
+  if (wgs_per_cu) *wgs_per_cu = reduce_wgs_per_cu(grad_dtype == ZR_BF16, fused != 0, world);
+  if (weighted) *weighted = xcd_weighted(world) ? 1 : 0;
+  return ZR_OK;
 }
 
 extern "C" zr_status zr_reduce_scatter_local(const zr_plan* plan, int32_t group,

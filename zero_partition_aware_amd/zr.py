@@ -96,6 +96,7 @@ _sigs = {
     "zr_plan_param_buckets": (c_i32, [c_vp, c_i64, _P(c_i64), _P(c_i64)]),
     "zr_plan_reduce_launches": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
                                         c_i32, _P(c_i64), _P(c_i64)]),
+    "zr_reduce_launch_occupancy": (c_i32, [c_i32, c_i32, c_i32, _P(c_i32), _P(c_i32)]),
     "zr_ipg_accumulate": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
                                   c_i64, c_i64, c_vp]),
     "zr_ipg_accumulate_first": (c_i32, [c_vp, _P(c_i64), _P(c_vp), c_i64, c_i32, c_vp,
@@ -396,6 +397,18 @@ def zr_plan_reduce_launches(plan, group, bucket_first, bucket_count, dst, grad_d
                                         dt, int(bool(fused)), int(bool(with_grad_out)),
                                         ctypes.byref(t), ctypes.byref(n)))
     return t.value, n.value
+
+
+def zr_reduce_launch_occupancy(grad_dtype, fused, world):
+    """(workgroups per CU, xcd_weighted) of an uncapped reduce call over
+    ``world`` replicas of grad_dtype ("bf16", "fp32" or a torch dtype):
+    workgroups per CU 0 = as many as the registers allow; xcd_weighted True
+    when the odd XCDs take 31/32 of the even XCDs' tiles."""
+    dt = _dtype_name_code(grad_dtype)
+    k, w = c_i32(), c_i32()
+    _check(_lib.zr_reduce_launch_occupancy(dt, int(bool(fused)), _i32(world, "world"),
+                                           ctypes.byref(k), ctypes.byref(w)))
+    return k.value, bool(w.value)
 
 
 def zr_plan_slices(plan, bucket=-1):
