@@ -1315,11 +1315,13 @@ std::atomic<int> g_lds_per_cu[64];  // per device, 0 until first queried
 //     14 6.27, 13 6.32, 11 6.14
 //   fp32 fused, R = 2 (MoE expert share): 18 -> 6.24; none 6.11, 20 6.23,
 //     17 6.25, 16 6.25; its range calls as buckets complete 18 -> 6.15
-//     against 6.05
-// The fp32 reduce-scatter at R = 2 takes none: 28 per CU gave +7% on the
-// whole MoE expert share (6.67 against 6.22) but -4.5% on the same share's
-// range calls as buckets complete (5.88 against 6.15).  Other replica counts
-// and types were not measured and take no cap.
+//     against 6.05; rechecked once 2 replicas took the XCD-weighted order:
+//     18 -> 6.42, none 6.31, 20 6.42, 16 6.42
+// The fp32 reduce-scatter at R = 2 takes none: in equal XCD shares 28 per CU
+// gave +7% on the whole MoE expert share but -4.5% on the same share's range
+// calls as buckets complete; in the weighted order 28 gave -1.3% on the
+// whole share and 24 -9%.  Other replica counts and types were not measured
+// and take no cap.
 int reduce_wgs_per_cu(bool bf16, bool fused, int R) {
   if (!ZR_RED_WGS_CAP) return 0;
   if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
