@@ -46,7 +46,9 @@
  *     call may enqueue several kernel launches: selections whose traffic
  *     exceeds about 2 GiB are cut into equal launches of at most that much
  *     (in one long launch the GPU's XCDs drift apart in the address space,
- *     which costs bandwidth; a launch boundary realigns them).
+ *     which costs bandwidth; a launch boundary realigns them).  Reduce
+ *     launches may reserve LDS they never touch, to hold each CU to a
+ *     measured number of their workgroups (zr_reduce_launch_occupancy).
  *   - Every call returns a zr_status.  Arguments are validated before any
  *     work is enqueued; on failure no output is touched and zr_last_error()
  *     returns a message (thread-local).  No C++ exception crosses the ABI.
