@@ -50,11 +50,14 @@ int g_failures = 0;
   } while (0)
 
 // Workgroups per CU an uncapped reduce launch is held to (0 = no cap), as
-// the library states it: fp32 fused 8, bf16 fused 6, bf16 reduce-scatter 20,
-// fp32 reduce-scatter 12 at 8 replicas; fp32 fused 18 at 2 replicas; no
-// other shape.
+// the library states it: at 8 replicas fp32 fused 8, bf16 fused 6, bf16
+// reduce-scatter 20, fp32 reduce-scatter 12; at 4 replicas fp32 fused 14,
+// bf16 fused 7; at 16 replicas fp32 fused 6, fp32 reduce-scatter 7; at 2
+// replicas fp32 fused 18; no other shape.
 int want_wgs_per_cu(bool bf16, bool fused, int R) {
   if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
+  if (R == 4 && fused) return bf16 ? 7 : 14;
+  if (R == 16 && !bf16) return fused ? 6 : 7;
   if (R == 2 && !bf16 && fused) return 18;
   return 0;
 }

@@ -425,12 +425,17 @@ def test_reduce_launch_shape_follows_the_stated_rules():
 def test_reduce_launch_occupancy_follows_the_stated_table():
     """zr_reduce_launch_occupancy against the table the library states: at
     8 replicas fp32 fused 8, bf16 fused 6, bf16 reduce-scatter 20, fp32
-    reduce-scatter 12 workgroups per CU; at 2 replicas fp32 fused 18; every
-    other shape 0 (register-limited); the XCD-weighted order from 2 replicas
-    up."""
+    reduce-scatter 12 workgroups per CU; at 4 replicas fp32 fused 14, bf16
+    fused 7; at 16 replicas fp32 fused 6, fp32 reduce-scatter 7; at 2
+    replicas fp32 fused 18; every other shape 0 (register-limited); the
+    XCD-weighted order from 2 replicas up."""
     def rule(bf16, fused, world):
         if world == 8:
             return (6 if bf16 else 8) if fused else (20 if bf16 else 12)
+        if world == 4 and fused:
+            return 7 if bf16 else 14
+        if world == 16 and not bf16:
+            return 6 if fused else 7
         if world == 2 and not bf16 and fused:
             return 18
         return 0

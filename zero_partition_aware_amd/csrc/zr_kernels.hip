@@ -1317,14 +1317,28 @@ std::atomic<int> g_lds_per_cu[64];  // per device, 0 until first queried
 //     17 6.25, 16 6.25; its range calls as buckets complete 18 -> 6.15
 //     against 6.05; rechecked once 2 replicas took the XCD-weighted order:
 //     18 -> 6.42, none 6.31, 20 6.42, 16 6.42
+//   fp32 fused, R = 4 (one 125M-element share): 14 -> 6.38 and 6.42 (two
+//     machines); none 6.20 and 6.22, 16 6.31 and 6.35, 13 6.43, 12 6.37 and
+//     6.38, 11 6.13, 10 5.97
+//   bf16 fused, R = 4 (one 62.5M-element share): 7 -> 6.34 and 6.38; none
+//     6.06 and 6.04, 9 6.26, 8 6.33 and 6.34, 6 6.37 and 6.38, 5 6.29
+//   fp32 fused, R = 16 (one 31.25M-element share): 6 -> 6.24 and 6.27; none
+//     6.06 and 6.06, 9 6.14, 8 6.18, 7 6.22, 5 6.17 and 6.19, 4 5.60
+//   fp32 reduce-scatter, R = 16 (same share): 7 -> 6.65; none 6.25 and
+//     6.24, 9 6.49, 8 6.54 and 6.59, 6 6.59 and 6.62, 5 6.10
+//   (At an eighth of those shares the four gain 0.8-1.9%; at a 32nd, where
+//   launches are a few microseconds, they are within +-1% of none.)
 // The fp32 reduce-scatter at R = 2 takes none: in equal XCD shares 28 per CU
 // gave +7% on the whole MoE expert share but -4.5% on the same share's range
 // calls as buckets complete; in the weighted order 28 gave -1.3% on the
-// whole share and 24 -9%.  Other replica counts and types were not measured
-// and take no cap.
+// whole share and 24 -9%.  The reduce-scatter at R = 4 (fp32 +0.6%, bf16
+// none) and the bf16 fused step at R = 16 (+0.7-1.0%) take none either;
+// other replica counts were not measured and take no cap.
 int reduce_wgs_per_cu(bool bf16, bool fused, int R) {
   if (!ZR_RED_WGS_CAP) return 0;
   if (R == 8) return fused ? (bf16 ? 6 : 8) : (bf16 ? 20 : 12);
+  if (R == 4 && fused) return bf16 ? 7 : 14;
+  if (R == 16 && !bf16) return fused ? 6 : 7;
   if (R == 2 && !bf16 && fused) return 18;
   return 0;
 }
