@@ -1,7 +1,7 @@
 """Large rank selections of one to three segments -- one slice, a slice plus
 the last partition's padding, a share cut by a bucket border -- checked on
-every element against the oracle, fused and unfused, bf16 and fp32, with 4
-and 8 replicas (both in the XCD-weighted order), including
+every element against the oracle, fused and unfused, bf16 and fp32, with 4,
+8 and 16 replicas (all in the XCD-weighted order), including
 selections cut into several launches (a launch carries at most ~2 GiB of
 traffic).  Reduced gradients bit-exact; Adam within rel 1e-6 / abs 1e-7 (v
 relative only); bf16 param = RNE of the kernel's own master.
@@ -131,6 +131,16 @@ def test_eight_replicas_weighted_order(is_bf16):
     # 8 replicas of 8,389,000 elements, fused and not
     _run([8 * 8_389_000], 8, 1 << 40, 5, is_bf16, True, 4, 1, 1)
     _run([8 * 8_389_000], 8, 1 << 40, 6, is_bf16, False, 5, 1, 1)
+    _free()
+
+
+@pytest.mark.parametrize("is_bf16", [False, True])
+def test_sixteen_replicas(is_bf16):
+    # 16 replicas of 4,000,000 elements (15,626 tiles of 256, 7,813 of 512),
+    # fused and not: the generic-replica fused kernel and the 16-replica
+    # reduce-scatter, at the sizes the workgroups-per-CU table covers
+    _run([16 * 4_000_000], 16, 1 << 40, 9, is_bf16, True, 8, 1, 1)
+    _run([16 * 4_000_000], 16, 1 << 40, 14, is_bf16, False, 9, 1, 1)
     _free()
 
 
