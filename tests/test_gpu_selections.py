@@ -137,8 +137,7 @@ def test_eight_replicas_weighted_order(is_bf16):
 @pytest.mark.parametrize("is_bf16", [False, True])
 def test_sixteen_replicas(is_bf16):
     # 16 replicas of 4,000,000 elements (15,626 tiles of 256, 7,813 of 512),
-    # fused and not: the generic-replica fused kernel and the 16-replica
-    # reduce-scatter, at the sizes the workgroups-per-CU table covers
+    # fused and not, in the 16-replica kernels
     _run([16 * 4_000_000], 16, 1 << 40, 9, is_bf16, True, 8, 1, 1)
     _run([16 * 4_000_000], 16, 1 << 40, 14, is_bf16, False, 9, 1, 1)
     _free()
