@@ -1727,6 +1727,10 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
   bool dword = false;
   for (int i = 0; i < nseg && !dword; ++i) dword = !slot_phase_exists((*hs)[i]);
   const int64_t nl = launches_for(total, reduce_tile_bytes(tile, gi.world, s, fused, gout));
+  // Queried before anything is enqueued (the staging launch included).
+  unsigned lds = 0;
+  st = reduce_lds_bytes(device, fused, dt == ZR_BF16, gi.world, max_wgs > 0, &lds);
+  if (st != ZR_OK) return st;
   if (noalloc) {
     Seg* table = nullptr;
     st = scratch_for(device, &table);
@@ -1738,9 +1742,6 @@ zr_status run_reduce(const zr_plan* plan, int32_t group, int64_t first, int64_t 
     st = get_dev_table(plan, kReduceTable, group, first, last, dst, tile, device, *hs, &a.segs);
     if (st != ZR_OK) return st;
   }
-  unsigned lds = 0;
-  st = reduce_lds_bytes(device, fused, dt == ZR_BF16, gi.world, max_wgs > 0, &lds);
-  if (st != ZR_OK) return st;
   for (int64_t i = 0; i < nl; ++i) {
     a.tile_base = launch_first(total, nl, i);
     a.tile_end = launch_first(total, nl, i + 1);
